@@ -1,0 +1,82 @@
+"""The routed experts forward in fp64 (test infrastructure only).
+
+What the pages fix:
+
+* bitsandbytes issue #1849, *Description*: the experts module holds
+  ``gate_up_proj [E, 2I, H]`` and ``down_proj [E, H, I]`` with an activation
+  ``act_fn`` applied between them; each ``[e]`` slice is an ``[out, in]``
+  weight (the maintainer thread names the stack
+  ``[num_experts, out_features, in_features]``).
+* unsloth-zoo issue #850, *Suggested fix*: the forward takes
+  ``(hidden_states, top_k_index, top_k_weights)``.
+* bitsandbytes issue #1849, maintainer thread: the correctness-first forward
+  dequantizes each expert and multiplies, expert by expert.
+
+Readings taken here (the pages leave them open):
+
+* The first I rows of ``gate_up_proj[e]`` are the gate, the last I the up
+  projection (the order in the name ``gate_up``).
+* The activation is SiLU, ``h = silu(g) * u`` with ``silu(z) = z / (1 + exp(-z))``.
+* ``top_k_weights`` are used as given (no renormalisation); a token's output
+  is ``sum_k w[t, k] * down[e_k] @ h_{t,k}``.  A repeated expert within a
+  token's row counts once per occurrence.
+* Everything is computed in fp64 from the dequantized bf16 weights and the
+  bf16 hidden states, so the result is the exact value the GPU's fp32
+  accumulation approximates.
+"""
+
+import numpy as np
+
+from .bf16 import bf16_to_f32
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
+    """Routed experts forward.
+
+    ``hidden_bits`` uint16 bf16 ``[T, H]``; ``top_k_index`` int ``[T, K]``;
+    ``top_k_weights`` float32 ``[T, K]``; ``gate_up[e]`` -> uint16 bf16
+    ``[2I, H]`` and ``down[e]`` -> uint16 bf16 ``[H, I]`` for each expert
+    (a 3-D array or any object with ``len`` and indexable by expert).  An
+    index outside ``[0, E)`` is not routed and contributes nothing.  Returns
+    fp64 ``[T, H]``.
+    """
+    x = bf16_to_f32(hidden_bits).astype(np.float64)
+    idx = np.asarray(top_k_index, dtype=np.int64)
+    wts = np.asarray(top_k_weights, dtype=np.float32).astype(np.float64)
+    T, H = x.shape
+    K = idx.shape[1]
+    y = np.zeros((T, K, H), dtype=np.float64)
+
+    E = len(gate_up)
+    for e in np.unique(idx):
+        if e < 0 or e >= E:                         # not routed: contributes nothing
+            continue
+        tok, kk = np.nonzero(idx == e)              # every (t, k) served by expert e
+        w_gu = bf16_to_f32(gate_up[int(e)]).astype(np.float64)   # [2I, H]
+        w_d = bf16_to_f32(down[int(e)]).astype(np.float64)       # [H, I]
+        I = w_gu.shape[0] // 2
+        assert w_gu.shape == (2 * I, H) and w_d.shape == (H, I)
+        X = x[tok]                                  # [n, H]
+        g = X @ w_gu[:I].T                          # gate: first I rows
+        u = X @ w_gu[I:].T                          # up: last I rows
+        h = silu(g) * u                             # [n, I]
+        y[tok, kk] = h @ w_d.T                      # [n, H]
+
+    out = np.zeros((T, H), dtype=np.float64)
+    for k in range(K):
+        out += wts[:, k:k + 1] * y[:, k]
+    return out
+
+
+def rel_frobenius(approx, exact):
+    """||approx - exact||_F / ||exact||_F in fp64."""
+    a = np.asarray(approx, dtype=np.float64)
+    b = np.asarray(exact, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
