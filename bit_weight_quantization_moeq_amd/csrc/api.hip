@@ -1,0 +1,211 @@
+// C ABI of libmoeq: host-side validation, workspace layout and dispatch.
+// Every check runs before the first HIP call, so a rejected call has no side
+// effect; nothing is ever skipped silently (the silent-skip and
+// packed-uint8-reaches-float-kernel failures described in bitsandbytes issue
+// #1849 and unsloth-zoo issue #850 are what these checks exist to prevent).
+#include <string.h>
+
+#include "moeq_internal.h"
+
+using namespace moeq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape / format validation of one qweight descriptor.
+moeq_status check_qweight(const moeq_qweight* q, int32_t want_format /* 0 = any */) {
+  if (!q) return MOEQ_EINVAL;
+  if (q->format != MOEQ_FMT_NF4 && q->format != MOEQ_FMT_INT8_ROWWISE) return MOEQ_EFORMAT;
+  if (want_format && q->format != want_format) return MOEQ_EFORMAT;
+  if (q->num_experts <= 0 || q->rows <= 0 || q->cols <= 0) return MOEQ_EINVAL;
+  if (!q->qdata || !q->scales) return MOEQ_EINVAL;
+  if (q->format == MOEQ_FMT_NF4) {
+    if (q->blocksize != MOEQ_NF4_BLOCKSIZE || q->cols % MOEQ_NF4_BLOCKSIZE != 0) return MOEQ_EBLOCK;
+  } else {
+    if (q->blocksize != q->cols) return MOEQ_EBLOCK;
+    if (q->cols % 8 != 0) return MOEQ_ESHAPE;
+  }
+  if (!aligned16(q->qdata) || !aligned16(q->scales)) return MOEQ_EALIGN;
+  return MOEQ_OK;
+}
+
+int64_t numel(const moeq_qweight* q) { return (int64_t)q->num_experts * q->rows * q->cols; }
+
+moeq_status device_status(hipError_t e) { return e == hipSuccess ? MOEQ_OK : MOEQ_EDEVICE; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t chunk_counts, chunk_base, rank, counts, offsets, tile_start, perm, slot, h, y, total;
+};
+
+// Workspace carve-up for n = T*K assignments over E experts (h/y only when
+// the forward needs them).
+Layout layout(int64_t n, int32_t E, int64_t I, int64_t H) {
+  Layout L{};
+  const int64_t nchunk = route_chunks(n);
+  size_t o = 0;
+  L.chunk_counts = o; o += up(sizeof(int32_t) * (size_t)(nchunk * E));
+  L.chunk_base = o;   o += up(sizeof(int32_t) * (size_t)(nchunk * E));
+  L.rank = o;         o += up(sizeof(int32_t) * (size_t)n);
+  L.counts = o;       o += up(sizeof(int32_t) * (size_t)E);
+  L.offsets = o;      o += up(sizeof(int32_t) * (size_t)(E + 1));
+  L.tile_start = o;   o += up(sizeof(int32_t) * (size_t)(E + 1));
+  L.perm = o;         o += up(sizeof(int32_t) * (size_t)n);
+  L.slot = o;         o += up(sizeof(int32_t) * (size_t)n);
+  L.h = o;            o += up(sizeof(uint16_t) * (size_t)(n * I));
+  L.y = o;            o += up(sizeof(float) * (size_t)(n * H));
+  L.total = o;
+  return L;
+}
+
+RouteBuffers route_buffers(void* ws, const Layout& L) {
+  char* b = static_cast<char*>(ws);
+  RouteBuffers r;
+  r.chunk_counts = reinterpret_cast<int32_t*>(b + L.chunk_counts);
+  r.chunk_base = reinterpret_cast<int32_t*>(b + L.chunk_base);
+  r.rank = reinterpret_cast<int32_t*>(b + L.rank);
+  r.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  r.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  r.tile_start = reinterpret_cast<int32_t*>(b + L.tile_start);
+  r.perm = reinterpret_cast<int32_t*>(b + L.perm);
+  r.slot = reinterpret_cast<int32_t*>(b + L.slot);
+  return r;
+}
+
+constexpr int64_t kMaxAssignments = int64_t(1) << 24;
+
+moeq_status check_forward_shapes(int32_t T, int32_t K, const moeq_qweight* gu, const moeq_qweight* dn) {
+  if (T < 0 || K < 1) return MOEQ_EINVAL;
+  moeq_status st = check_qweight(gu, 0);
+  if (st != MOEQ_OK) return st;
+  st = check_qweight(dn, 0);
+  if (st != MOEQ_OK) return st;
+  if (gu->format != dn->format) return MOEQ_EFORMAT;
+  if (gu->num_experts != dn->num_experts) return MOEQ_ESHAPE;
+  if (gu->num_experts > MOEQ_MAX_EXPERTS) return MOEQ_ESHAPE;
+  if (gu->rows % 2 != 0) return MOEQ_ESHAPE;
+  const int32_t I = gu->rows / 2, H = gu->cols;
+  if (dn->rows != H || dn->cols != I) return MOEQ_ESHAPE;
+  if (H % 64 != 0 || I % 64 != 0) return MOEQ_ESHAPE;
+  if ((int64_t)T * K > kMaxAssignments) return MOEQ_ESHAPE;
+  return MOEQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moeq_abi_version(void) { return MOEQ_ABI_VERSION; }
+
+const char* moeq_status_string(moeq_status s) {
+  switch (s) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_EINVAL: return "invalid argument (null pointer, non-positive dimension, K < 1 or T < 0)";
+    case MOEQ_ESHAPE: return "inconsistent or unsupported shapes";
+    case MOEQ_EBLOCK: return "blocksize rule violated (NF4: blocksize 64 and cols % 64 == 0; int8: blocksize == cols)";
+    case MOEQ_EFORMAT: return "format tag not what the call needs, or gate_up and down formats differ";
+    case MOEQ_EALIGN: return "pointer not 16-byte aligned";
+    case MOEQ_EWORKSPACE: return "workspace missing or too small";
+    case MOEQ_EDEVICE: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+moeq_status moeq_nf4_codebook(float* out) {
+  if (!out) return MOEQ_EINVAL;
+  for (int i = 0; i < 16; ++i) memcpy(&out[i], &kNf4LevelBits[i], sizeof(float));
+  return MOEQ_OK;
+}
+
+moeq_status moeq_quantize_nf4(const uint16_t* w, const moeq_qweight* dst, void* stream) {
+  moeq_status st = check_qweight(dst, MOEQ_FMT_NF4);
+  if (st != MOEQ_OK) return st;
+  if (!w) return MOEQ_EINVAL;
+  if (!aligned16(w)) return MOEQ_EALIGN;
+  const int64_t nblocks = numel(dst) / kNf4Block;
+  return device_status(launch_quantize_nf4(w, static_cast<uint8_t*>(dst->qdata), dst->scales, nblocks,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moeq_status moeq_quantize_int8_rowwise(const uint16_t* w, const moeq_qweight* dst, void* stream) {
+  moeq_status st = check_qweight(dst, MOEQ_FMT_INT8_ROWWISE);
+  if (st != MOEQ_OK) return st;
+  if (!w) return MOEQ_EINVAL;
+  if (!aligned16(w)) return MOEQ_EALIGN;
+  const int64_t nrows = (int64_t)dst->num_experts * dst->rows;
+  return device_status(launch_quantize_int8(w, static_cast<int8_t*>(dst->qdata), dst->scales, nrows,
+                                            dst->cols, static_cast<hipStream_t>(stream)));
+}
+
+moeq_status moeq_dequantize(const moeq_qweight* src, uint16_t* out, void* stream) {
+  moeq_status st = check_qweight(src, 0);
+  if (st != MOEQ_OK) return st;
+  if (!out) return MOEQ_EINVAL;
+  if (!aligned16(out)) return MOEQ_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (src->format == MOEQ_FMT_NF4)
+    return device_status(launch_dequantize_nf4(static_cast<const uint8_t*>(src->qdata), src->scales, out,
+                                               numel(src) / kNf4Block, s));
+  return device_status(launch_dequantize_int8(static_cast<const int8_t*>(src->qdata), src->scales, out,
+                                              (int64_t)src->num_experts * src->rows, src->cols, s));
+}
+
+size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qweight* gu,
+                                            const moeq_qweight* dn) {
+  if (check_forward_shapes(T, K, gu, dn) != MOEQ_OK) return 0;
+  return layout((int64_t)T * K, gu->num_experts, gu->rows / 2, gu->cols).total;
+}
+
+moeq_status moeq_experts_forward(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T, int32_t K,
+                                 const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  moeq_status st = check_forward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !idx || !wts || !out) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const Layout L = layout((int64_t)T * K, E, I, H);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  if (!aligned16(workspace)) return MOEQ_EALIGN;
+
+  ForwardArgs a;
+  a.x = x; a.idx = idx; a.wts = wts;
+  a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
+  a.format = gu->format;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales;
+  a.out = out;
+  a.rb = route_buffers(workspace, L);
+  a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
+  a.y = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.y);
+  return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E) {
+  if (T < 0 || K < 1 || E < 1 || E > MOEQ_MAX_EXPERTS || (int64_t)T * K > kMaxAssignments) return 0;
+  return layout((int64_t)T * K, E, 0, 0).total;
+}
+
+moeq_status moeq_route_buckets(const int32_t* idx, int32_t T, int32_t K, int32_t E, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, int32_t* slot, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 1 || E < 1) return MOEQ_EINVAL;
+  if (E > MOEQ_MAX_EXPERTS || (int64_t)T * K > kMaxAssignments) return MOEQ_ESHAPE;
+  if (!counts || !offsets || (T > 0 && (!idx || !perm || !slot))) return MOEQ_EINVAL;
+  const int64_t n = (int64_t)T * K;
+  const Layout L = layout(n, E, 0, 0);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  RouteBuffers rb = route_buffers(workspace, L);
+  // The caller's arrays replace the workspace ones for the four outputs.
+  rb.counts = counts;
+  rb.offsets = offsets;
+  rb.perm = perm;
+  rb.slot = slot;
+  return device_status(launch_route(idx, (int32_t)n, E, forward_tile_rows(), rb, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

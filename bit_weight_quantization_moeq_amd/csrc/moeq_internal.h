@@ -1,0 +1,94 @@
+// Internal declarations shared by the libmoeq HIP translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moeq.h"
+
+namespace moeq {
+
+// ---------------------------------------------------------------------------
+// NF4 constants (frozen).  The pages name the NF4 format ("MoE Expert
+// Quantization", Implementation details) without printing its levels; these
+// are the QLoRA NormalFloat levels: standard-normal quantiles at evenly
+// spaced probabilities from delta = ((1-1/30)+(1-1/32))/2 towards 1/2, 8 on
+// the positive side and 7 on the negative side plus an exact zero, divided
+// by the largest magnitude, formed in fp64 and rounded once to fp32.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNf4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+// Decision thresholds: t_i is the largest fp32 not above the exact midpoint
+// (level_i + level_{i+1}) / 2.  With n = fp32(w / absmax), the nearest level
+// (ties to the lower one) is #{i : n > t_i}.  For bf16 w and absmax a > 0 the
+// kernels evaluate n > t_i without the division, as the exact test
+// w >= a * t_i (the sign of fma(a, t_i, -w)); the two agree on every pair of
+// bf16 values, which an exhaustive enumeration of all bf16 ratios confirms
+// (no bf16 ratio falls between t_i and the rounding boundary above it).
+constexpr uint32_t kNf4ThresholdBits[15] = {
+    0xbf591cd9u, 0xbf1c5270u, 0xbeeb847du, 0xbeadea75u, 0xbe703ceau,
+    0xbe0d38b9u, 0xbd3a7869u, 0x3d22fb01u, 0x3df6485fu, 0x3e5067dcu,
+    0x3e9582d1u, 0x3ec753f5u, 0x3f006d01u, 0x3f248dacu, 0x3f5c89d8u};
+
+constexpr int kNf4Block = 64;
+constexpr int kNf4ZeroCode = 7;
+
+// The NF4 decision in the kernels first picks a bucket of width 1/16 in n
+// from an approximate ratio, then makes one exact threshold test.  Bucket j
+// covers n in [(j-17)/16, (j-16)/16); every bucket holds at most one
+// threshold and no threshold lies within 1e-3 of a bucket edge, so an
+// approximate ratio that strays into a neighbouring bucket still yields the
+// same code.  Entry: {threshold to test (2.0 when the bucket has none),
+// number of thresholds below the bucket}.
+constexpr int kNf4Buckets = 34;
+
+// ---------------------------------------------------------------------------
+// Launch helpers (host side), one per translation unit's kernels.
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_nf4(const uint16_t* w, uint8_t* q, float* absmax, int64_t nblocks,
+                               hipStream_t s);
+hipError_t launch_quantize_int8(const uint16_t* w, int8_t* q, float* scale, int64_t nrows,
+                                int32_t cols, hipStream_t s);
+hipError_t launch_dequantize_nf4(const uint8_t* q, const float* absmax, uint16_t* out,
+                                 int64_t nblocks, hipStream_t s);
+hipError_t launch_dequantize_int8(const int8_t* q, const float* scale, uint16_t* out,
+                                  int64_t nrows, int32_t cols, hipStream_t s);
+
+// Routing workspace carve-up (all int32).
+struct RouteBuffers {
+  int32_t* chunk_counts;  // [nchunk][E]
+  int32_t* chunk_base;    // [nchunk][E]
+  int32_t* rank;          // [n]
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* tile_start;    // [E+1] (prefix sum of ceil(counts / tile_rows))
+  int32_t* perm;          // [n]
+  int32_t* slot;          // [n]
+};
+constexpr int kRouteChunk = 256;
+int64_t route_chunks(int64_t n);
+hipError_t launch_route(const int32_t* idx, int32_t n, int32_t E, int32_t tile_rows,
+                        const RouteBuffers& b, hipStream_t s);
+
+struct ForwardArgs {
+  const uint16_t* x;        // [T][H]
+  const int32_t* idx;       // [T][K]
+  const float* wts;         // [T][K]
+  int32_t T, K, E, H, I;
+  int32_t format;
+  const void* gu_q;         // gate_up codes
+  const float* gu_s;        // gate_up scales
+  const void* dn_q;         // down codes
+  const float* dn_s;        // down scales
+  uint16_t* out;            // [T][H]
+  RouteBuffers rb;
+  uint16_t* h;              // [T*K][I] bf16, expert-sorted rows
+  float* y;                 // [T*K][H] fp32, expert-sorted rows
+};
+hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s);
+int32_t forward_tile_rows();
+
+}  // namespace moeq

@@ -1,0 +1,186 @@
+/*
+ * moeq.h -- C ABI of libmoeq: NF4 / row-wise int8 quantization of fused MoE
+ * expert tensors and the routed experts forward straight from the packed
+ * storage, on AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer to caller-owned memory.  The
+ *   library allocates nothing and keeps no state between calls.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *   stream).  MOEQ_OK means validation passed and every kernel was enqueued;
+ *   a HIP launch error maps to MOEQ_EDEVICE.  No call synchronises the host.
+ * - All validation happens on the host before any HIP call, so a rejected
+ *   call has no side effect.  No call ever no-ops silently on bad input: the
+ *   pages describe expert tensors silently left unquantized, and a packed
+ *   uint8 tensor silently reaching a float kernel, as the failures to avoid
+ *   (bitsandbytes issue #1849, comment thread; unsloth-zoo issue #850).
+ * - Tensors are row-major and contiguous.  An expert tensor is
+ *   [E][rows][cols] with each [e] slice an [out_features, in_features]
+ *   weight: gate_up_proj is [E][2I][H] and down_proj is [E][H][I]
+ *   (bitsandbytes issue #1849, Description code and maintainer thread).
+ * - bf16 values travel as their uint16_t bit patterns.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEQ_ABI_VERSION 1
+#define MOEQ_NF4_BLOCKSIZE 64
+#define MOEQ_MAX_EXPERTS 1024
+
+typedef int32_t moeq_status;
+enum {
+  MOEQ_OK = 0,
+  MOEQ_EINVAL = -1,     /* null pointer, a dimension <= 0, K < 1, T < 0            */
+  MOEQ_ESHAPE = -2,     /* gate_up / down / hidden dimensions inconsistent          */
+  MOEQ_EBLOCK = -3,     /* NF4: blocksize != 64 or cols % 64 != 0; int8: blocksize != cols */
+  MOEQ_EFORMAT = -4,    /* format tag not what the call needs, or gate_up and down differ */
+  MOEQ_EALIGN = -5,     /* a pointer is not 16-byte aligned                          */
+  MOEQ_EWORKSPACE = -6, /* workspace null or smaller than moeq_experts_forward_workspace_bytes */
+  MOEQ_EDEVICE = -7     /* a HIP call failed                                         */
+};
+
+enum { MOEQ_FMT_NF4 = 1, MOEQ_FMT_INT8_ROWWISE = 2 };
+
+/*
+ * A quantized expert tensor [E][rows][cols] in caller-owned device memory.
+ *
+ * NF4 (format MOEQ_FMT_NF4, blocksize 64; "MoE Expert Quantization",
+ * Implementation details: 4-bit mode is NF4; bitsandbytes issue #1849,
+ * maintainer thread: plain packed storage plus a module-owned absmax
+ * [num_experts, blocks_per_expert], in_features divisible by the blocksize):
+ *   qdata  uint8 [E][rows][cols/2]; column 2m in the high nibble of byte m,
+ *          column 2m+1 in the low nibble.
+ *   scales fp32 [E][rows*cols/64]: the absmax of each 64-element block along
+ *          a row, blocks in row order.
+ * int8 row-wise (format MOEQ_FMT_INT8_ROWWISE, blocksize == cols;
+ * "MoE Expert Quantization", Implementation details: 8-bit mode is a
+ * row-wise int8 parametrization):
+ *   qdata  int8 [E][rows][cols], codes in [-127, 127].
+ *   scales fp32 [E][rows]: absmax(row) / 127.
+ * Since blocks never straddle an expert, &qdata[e] / &scales[e] with
+ * num_experts = 1 describe expert e alone.
+ */
+typedef struct moeq_qweight {
+  int32_t format;
+  int32_t num_experts;
+  int32_t rows;
+  int32_t cols;
+  int32_t blocksize;
+  void *qdata;
+  float *scales;
+} moeq_qweight;
+
+/* Version of this ABI (MOEQ_ABI_VERSION). */
+int32_t moeq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *moeq_status_string(moeq_status status);
+
+/*
+ * Host copy of the 16 NF4 levels the kernels use (ascending, fp32), written
+ * to out[0..15].  The pages name the NF4 format without printing it; the
+ * levels are the QLoRA NormalFloat construction (evenly spaced standard-
+ * normal quantiles, zero exactly representable, extremes -1 and +1).
+ * Host-only; makes no HIP call.  MOEQ_EINVAL if out is NULL.
+ */
+moeq_status moeq_nf4_codebook(float *out);
+
+/*
+ * Quantize-on-load, 4-bit ("MoE Expert Quantization", intro and
+ * Implementation details; bitsandbytes issue #1849, maintainer thread).
+ * w_bf16: bf16 [E][rows][cols] (16-byte aligned); dst describes the output
+ * and must have format MOEQ_FMT_NF4, blocksize 64, cols % 64 == 0, and
+ * 16-byte aligned qdata/scales.  For each 64-block: absmax = max |w|;
+ * n = fp32(w / absmax) (IEEE division); code = nearest NF4 level, an exact
+ * tie to the lower index; an all-zero block stores absmax 0 and code 7.
+ * The source may be freed (stream-ordered) as soon as the call returns.
+ * Preconditions not checked on device: finite weights.
+ */
+moeq_status moeq_quantize_nf4(const uint16_t *w_bf16, const moeq_qweight *dst, void *stream);
+
+/*
+ * Quantize-on-load, 8-bit ("MoE Expert Quantization", Implementation
+ * details: row-wise int8 parametrization).  dst: format
+ * MOEQ_FMT_INT8_ROWWISE, blocksize == cols, cols % 8 == 0.  Per row:
+ * absmax = max |w|; scale = fp32(absmax / 127); q = round-half-even of
+ * fp32(fp32(127 w) / absmax); a zero row gives scale 0 and q 0.
+ * Preconditions not checked on device: finite weights, |w| < 2^120.
+ */
+moeq_status moeq_quantize_int8_rowwise(const uint16_t *w_bf16, const moeq_qweight *dst, void *stream);
+
+/*
+ * Dequantize (bitsandbytes issue #1849, maintainer thread: the
+ * correctness-first path dequantizes the experts; "MoE Expert
+ * Quantization", Implementation details: int8 is dequantized for the
+ * forward).  out_bf16: bf16 [E][rows][cols], 16-byte aligned.
+ * NF4: out = bf16_rne(fp32(level[code] * absmax)); int8: out =
+ * bf16_rne(fp32(q * scale)) -- the fp32 product first, then round to bf16.
+ */
+moeq_status moeq_dequantize(const moeq_qweight *src, uint16_t *out_bf16, void *stream);
+
+/*
+ * Device workspace moeq_experts_forward needs for T tokens and top-K routing
+ * over these weights (an upper bound independent of the routing); 0 if the
+ * arguments are invalid.  Host-only.
+ */
+size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qweight *gate_up,
+                                            const moeq_qweight *down);
+
+/*
+ * Routed experts forward from packed storage (unsloth-zoo issue #850,
+ * Suggested fix: the (hidden_states, top_k_index, top_k_weights) interface
+ * is uniform across fused-expert architectures; bitsandbytes issue #1849,
+ * Description: gate_up_proj [E, 2I, H], down_proj [E, H, I], act_fn).
+ *   hidden_bf16   bf16 [T][H]
+ *   top_k_index   int32 [T][K]; entries outside [0, E) are not routed and
+ *                 contribute nothing; a repeated expert counts per occurrence
+ *   top_k_weights fp32 [T][K], used as given
+ *   gate_up       [E][2I][H]: rows 0..I-1 are the gate, rows I..2I-1 the up
+ *                 projection; down [E][H][I]; both NF4 or both int8
+ *   out_bf16      bf16 [T][H]:
+ *                 out[t] = sum_k w[t,k] * down[e] @ (silu(gate[e] x_t) * up[e] x_t)
+ *                 with the k terms added in order k = 0..K-1 (deterministic,
+ *                 bit-identical run to run).
+ *   workspace     device memory of at least
+ *                 moeq_experts_forward_workspace_bytes(T, K, gate_up, down).
+ * Weights are dequantized tile by tile inside the kernels (bf16 operands,
+ * fp32 accumulation); no dequantized tensor is materialised.  T == 0 is a
+ * valid no-op.  H and I must be multiples of 64 (MOEQ_ESHAPE otherwise).
+ */
+moeq_status moeq_experts_forward(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                 const float *top_k_weights, int32_t T, int32_t K,
+                                 const moeq_qweight *gate_up, const moeq_qweight *down,
+                                 uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * The routing stage of moeq_experts_forward on its own (same kernels):
+ * groups the T*K assignments a = t*K + k by expert (unsloth-zoo issue #850,
+ * Suggested fix: one generic routing for every architecture).
+ *   counts  int32 [E]    assignments per expert
+ *   offsets int32 [E+1]  exclusive prefix sum of counts
+ *   perm    int32 [T*K]  assignments sorted by expert, ascending a within an
+ *                        expert; entries past offsets[E] are left untouched
+ *   slot    int32 [T*K]  position of a in perm, -1 for an unrouted a
+ * Needs T*K <= 2^24 and E <= MOEQ_MAX_EXPERTS; workspace as for the forward
+ * (moeq_experts_forward_workspace_bytes with any weights of E experts) or
+ * moeq_route_workspace_bytes(T, K, E).
+ */
+size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E);
+moeq_status moeq_route_buckets(const int32_t *top_k_index, int32_t T, int32_t K, int32_t E,
+                               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *slot,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

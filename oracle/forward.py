@@ -44,14 +44,17 @@ def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
     ``[2I, H]`` and ``down[e]`` -> uint16 bf16 ``[H, I]`` for each expert
     (a 3-D array or any object with ``len`` and indexable by expert).  An
     index outside ``[0, E)`` is not routed and contributes nothing.  Returns
-    fp64 ``[T, H]``.
+    fp64 ``[T, H]``.  ``down[e]`` may hold only some rows of the down weight
+    (the same rows for every expert); the result then holds the matching
+    output columns, since output column n depends only on down row n.
     """
     x = bf16_to_f32(hidden_bits).astype(np.float64)
     idx = np.asarray(top_k_index, dtype=np.int64)
     wts = np.asarray(top_k_weights, dtype=np.float32).astype(np.float64)
     T, H = x.shape
     K = idx.shape[1]
-    y = np.zeros((T, K, H), dtype=np.float64)
+    n_out = None
+    y = None
 
     E = len(gate_up)
     for e in np.unique(idx):
@@ -61,14 +64,21 @@ def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
         w_gu = bf16_to_f32(gate_up[int(e)]).astype(np.float64)   # [2I, H]
         w_d = bf16_to_f32(down[int(e)]).astype(np.float64)       # [H, I]
         I = w_gu.shape[0] // 2
-        assert w_gu.shape == (2 * I, H) and w_d.shape == (H, I)
+        assert w_gu.shape == (2 * I, H) and w_d.shape[1] == I
         X = x[tok]                                  # [n, H]
         g = X @ w_gu[:I].T                          # gate: first I rows
         u = X @ w_gu[I:].T                          # up: last I rows
         h = silu(g) * u                             # [n, I]
-        y[tok, kk] = h @ w_d.T                      # [n, H]
+        if y is None:
+            n_out = w_d.shape[0]
+            y = np.zeros((T, K, n_out), dtype=np.float64)
+        y[tok, kk] = h @ w_d.T                      # [n, n_out]
 
-    out = np.zeros((T, H), dtype=np.float64)
+    if y is None:                                   # nothing routed
+        n_out = H if isinstance(down, np.ndarray) and down.ndim == 3 and down.shape[1] == H else (
+            down[0].shape[0] if len(down) else H)
+        y = np.zeros((T, K, n_out), dtype=np.float64)
+    out = np.zeros((T, n_out), dtype=np.float64)
     for k in range(K):
         out += wts[:, k:k + 1] * y[:, k]
     return out

@@ -1,0 +1,127 @@
+"""libmoeq on the host: it loads, exports every function include/moeq.h declares,
+rejects bad arguments before any HIP call, and its frozen NF4 constants equal
+the oracle's independent derivation.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_quantization_moeq_amd as moeq
+from oracle.nf4 import nf4_codebook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+INTERNAL = os.path.join(ROOT, "bit_weight_quantization_moeq_amd", "csrc", "moeq_internal.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moeq.library_path()),
+                                reason="libmoeq.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moeq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = ctypes.CDLL(moeq.library_path())
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert moeq.moeq_abi_version() == 1
+    for s in range(0, -8, -1):
+        assert moeq.moeq_status_string(s) != "unknown status"
+    assert moeq.moeq_status_string(-99) == "unknown status"
+
+
+def test_codebook_equals_oracle_derivation_bitwise():
+    lib_cb = np.array(moeq.moeq_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), nf4_codebook().view(np.uint32))
+
+
+def _kernel_thresholds():
+    text = open(INTERNAL).read()
+    body = re.search(r"kNf4ThresholdBits\[15\]\s*=\s*\{(.*?)\};", text, re.S).group(1)
+    return np.array([int(h, 16) for h in re.findall(r"0x([0-9a-fA-F]+)u", body)], np.uint32).view(np.float32)
+
+
+def test_kernel_thresholds_are_midpoints_rounded_down():
+    from fractions import Fraction
+    c = [Fraction(float(x)) for x in nf4_codebook()]
+    t = _kernel_thresholds()
+    assert t.shape == (15,)
+    for i in range(15):
+        mid = (c[i] + c[i + 1]) / 2
+        assert Fraction(float(t[i])) <= mid
+        assert Fraction(float(np.nextafter(t[i], np.float32(np.inf)))) > mid
+
+
+def test_kernel_bucket_layout_assumption():
+    # The kernel picks a 1/16-wide bucket from an approximate ratio and tests
+    # one threshold: each bucket must hold at most one threshold, none near an edge.
+    t = _kernel_thresholds().astype(np.float64)
+    pos = (t + 1.0) * 16.0
+    assert len(set(np.floor(pos).astype(int))) == 15
+    assert np.min(np.abs(pos - np.round(pos))) / 16.0 > 1e-3
+
+
+def _qw(fmt=1, E=1, R=4, C=64, bs=64, q=256, s=512):
+    return moeq._QW(fmt, E, R, C, bs, q, s)
+
+
+def _quant(qw, w=4096):
+    lib = moeq._load()
+    return lib.moeq_quantize_nf4(ctypes.c_void_p(w), ctypes.byref(qw), None)
+
+
+def test_nf4_validation_rejects_before_any_device_call():
+    lib = moeq._load()
+    assert _quant(_qw(C=96)) == -3                       # cols % 64 != 0
+    assert _quant(_qw(bs=32)) == -3                      # blocksize != 64
+    assert _quant(_qw(fmt=2, bs=64)) == -4               # int8 descriptor to the NF4 call
+    assert _quant(_qw(fmt=7)) == -4
+    assert _quant(_qw(E=0)) == -1
+    assert _quant(_qw(q=0)) == -1
+    assert _quant(_qw(), w=0) == -1
+    assert _quant(_qw(q=8)) == -5                        # misaligned codes
+    assert _quant(_qw(), w=4098) == -5                   # misaligned source
+    assert lib.moeq_quantize_nf4(ctypes.c_void_p(4096), None, None) == -1
+    qw = _qw(fmt=2, C=60, bs=60)
+    assert lib.moeq_quantize_int8_rowwise(ctypes.c_void_p(4096), ctypes.byref(qw), None) == -2
+    qw = _qw(fmt=2, C=64, bs=32)
+    assert lib.moeq_quantize_int8_rowwise(ctypes.c_void_p(4096), ctypes.byref(qw), None) == -3
+    assert lib.moeq_dequantize(ctypes.byref(_qw()), ctypes.c_void_p(0), None) == -1
+
+
+def test_forward_validation_and_workspace_sizing():
+    lib = moeq._load()
+    E, H, I = 4, 128, 64
+    gu = _qw(1, E, 2 * I, H, 64)
+    dn = _qw(1, E, H, I, 64)
+    ws = lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(dn))
+    assert ws >= 10 * 2 * (I * 2 + H * 4)
+    bad_dn = _qw(1, E, H, 2 * I, 64)                     # down cols != I
+    assert lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(bad_dn)) == 0
+    P = ctypes.c_void_p
+
+    def fwd(T, K, g, d, ws_ptr=4096, ws_bytes=ws, x=4096):
+        return lib.moeq_experts_forward(P(x), P(4096), P(4096), T, K, ctypes.byref(g), ctypes.byref(d),
+                                        P(4096), P(ws_ptr), ws_bytes, None)
+
+    assert fwd(10, 2, gu, bad_dn) == -2
+    assert fwd(10, 2, gu, _qw(2, E, H, I, I)) == -4      # mixed formats
+    assert fwd(10, 2, gu, _qw(1, E + 1, H, I, 64)) == -2
+    assert fwd(10, 0, gu, dn) == -1
+    assert fwd(-1, 2, gu, dn) == -1
+    assert fwd(0, 2, gu, dn) == 0                         # T == 0: valid no-op
+    assert fwd(10, 2, gu, dn, ws_bytes=ws - 1) == -6
+    assert fwd(10, 2, gu, dn, ws_ptr=0) == -6
+    assert fwd(10, 2, gu, dn, x=4100) == -5
+    assert lib.moeq_route_workspace_bytes(10, 2, 5000) == 0
