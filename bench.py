@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 MoE-experts hot path on one MI355X.
+
+One step = quantize-on-load of one OLMoE-1B-7B-shaped MoE layer (gate_up
+[64, 2048, 2048] and down [64, 2048, 1024] bf16 ~ N(0, 0.02) -> NF4,
+blocksize 64) followed by the routed experts forward of T = 4096 tokens with
+top-8 uniform routing straight from that packed storage (routing buckets,
+gate_up grouped GEMM + SwiGLU, down grouped GEMM, k-ordered combine).
+
+Printed (one JSON line): ``value`` = experts-forward tokens/s (HIP events
+around the forward of every timed step), ``quantize_GBps`` = quantize
+algorithmic bytes / quantize time (events), ``ms_per_step`` = wall time per
+whole step; ``roofline`` for the dominant kernel of the step, from its own
+events; ``decode`` = forward-only figures at T = 1 and 32; ``cpu_baseline`` =
+the CPU oracle on a bounded sample of the same workload.  Inputs are seeded
+synthetic tensors resident in HBM before the timed region.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NF4 experts-forward tokens/s + quantize GB/s, fraction of HBM/MFMA peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+NF4_BYTES_PER_ELEM = 2.0 + 0.5 + 4.0 / 64   # bf16 read + packed code + absmax share
+NF4_PACKED_BYTES_PER_ELEM = 0.5 + 4.0 / 64  # what the forward streams per weight element
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="olmoe")
+    ap.add_argument("--T", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def forward_bytes_flops(s, idx_np, T):
+    """Algorithmic bytes and flops of one forward: touched experts' packed weights
+    once, x in and out once, the routing inputs once; 6*T*K*H*I flops."""
+    U = len(set(idx_np.reshape(-1).tolist()))
+    wbytes = U * 3 * s.H * s.I * NF4_PACKED_BYTES_PER_ELEM
+    abytes = 2 * T * s.H * 2 + T * s.K * 8
+    flops = 6.0 * T * s.K * s.H * s.I
+    return wbytes + abytes, flops, U
+
+
+def new_events(torch, n):
+    """n timing events on torch's current stream, created now (one record each)
+    so their raw hipEvent_t handles can be handed to the library."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    return ev
+
+
+def cpu_baseline(s, gu, dn, x, idx, wts, T):
+    """The oracle, untuned, on a bounded sample: NF4 quantize of two experts'
+    gate_up and down, and the forward of T tokens with their expert indices
+    folded onto those two experts (identical work per assignment)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import moeq_synth as syn
+    from oracle.forward import experts_forward
+    from oracle.nf4 import nf4_dequantize, nf4_quantize
+
+    gbits = syn.bf16_bits(gu[:2])
+    dbits = syn.bf16_bits(dn[:2])
+    t0 = time.perf_counter()
+    qg = nf4_quantize(gbits)
+    qd = nf4_quantize(dbits)
+    tq = time.perf_counter() - t0
+    qelems = gbits.size + dbits.size
+    dg, dd = nf4_dequantize(*qg), nf4_dequantize(*qd)
+    Ts = min(T, 1024)
+    xs = syn.bf16_bits(x[:Ts])
+    ids = idx[:Ts].cpu().numpy() % 2
+    ws = wts[:Ts].cpu().numpy()
+    t0 = time.perf_counter()
+    experts_forward(xs, ids, ws, dg, dd)
+    tf = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": Ts / tf, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "quantize_GBps": qelems * NF4_BYTES_PER_ELEM / tq / 1e9,
+        "sample": (f"NF4 quantize of experts 0-1 of gate_up and down ({qelems} elements, {tq:.1f} s); "
+                   f"fp64 forward of the first {Ts} tokens of the T={T} top-{s.K} workload with expert "
+                   f"indices folded onto those two experts ({tf:.1f} s); numpy/BLAS threads={threads}, "
+                   f"host cpu_count={os.cpu_count()}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_weight_quantization_moeq_amd as moeq
+    import moeq_synth as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    s = syn.SHAPES[args.config]
+    T = args.T
+    if s.fmt != "nf4":
+        raise SystemExit("the benchmarked path is NF4")
+
+    gu = syn.expert_weights(s.gate_up_shape, tensor=syn.GATE_UP, outliers=s.outliers, device=dev)
+    dn = syn.expert_weights(s.down_shape, tensor=syn.DOWN, outliers=s.outliers, device=dev)
+    x = syn.hidden_states(T, s.H, device=dev)
+    idx, wts = syn.routing(T, s.K, s.E, kind=s.routing, device=dev)
+    qg = moeq.QWeight.empty(moeq.FMT_NF4, *s.gate_up_shape, device=dev)
+    qd = moeq.QWeight.empty(moeq.FMT_NF4, *s.down_shape, device=dev)
+    out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+    nsteps = args.warmup + args.steps
+    ev = [new_events(torch, 8) for _ in range(nsteps)]
+
+    def step(e):
+        # every library call runs on torch's current stream, where these events are recorded
+        e[0].record()
+        moeq.moeq_quantize_nf4(gu, out=qg)
+        e[1].record()
+        moeq.moeq_quantize_nf4(dn, out=qd)
+        e[2].record()
+        moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=out, workspace=ws,
+                                  stage_events=[h.cuda_event for h in e[3:8]])
+
+    for i in range(args.warmup):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    names = ["quantize_gate_up", "quantize_down", None, "route", "g1_gate_up_swiglu", "g2_down", "combine"]
+    stage = {n: [] for n in names if n}
+    fwd_ms, q_ms = [], []
+    for i in range(args.warmup, nsteps):
+        e = ev[i]
+        for j, n in enumerate(names):
+            if n:
+                stage[n].append(e[j].elapsed_time(e[j + 1]))
+        q_ms.append(e[0].elapsed_time(e[2]))
+        fwd_ms.append(e[3].elapsed_time(e[7]))
+    avg = {n: float(np.mean(v)) for n, v in stage.items()}
+    fwd = float(np.mean(fwd_ms))
+    qt = float(np.mean(q_ms))
+
+    n_gu, n_dn = int(np.prod(s.gate_up_shape)), int(np.prod(s.down_shape))
+    q_bytes = (n_gu + n_dn) * NF4_BYTES_PER_ELEM
+    idx_np = idx.cpu().numpy()
+    f_bytes, f_flops, U = forward_bytes_flops(s, idx_np, T)
+    n_assign = T * s.K
+
+    # dominant kernel of the step and its roofline (algorithmic work per launch / event time)
+    dom = max(avg, key=avg.get)
+    work = {
+        "quantize_gate_up": ("hbm", n_gu * NF4_BYTES_PER_ELEM),
+        "quantize_down": ("hbm", n_dn * NF4_BYTES_PER_ELEM),
+        "g1_gate_up_swiglu": ("mfma", 4.0 * n_assign * s.H * s.I),
+        "g2_down": ("mfma", 2.0 * n_assign * s.H * s.I),
+        "route": ("hbm", n_assign * 4 * 4.0),
+        "combine": ("hbm", n_assign * s.H * 4.0 + T * s.H * 2.0),
+    }
+    bound, amount = work[dom]
+    if bound == "hbm":
+        achieved = amount / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+    else:
+        achieved = amount / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = avg[dom]
+
+    result = {
+        "metric": METRIC,
+        "value": T / (fwd * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"{s.name}-shaped MoE layer E={s.E} H={s.H} I={s.I} top-{s.K} "
+                                f"{s.routing} routing, T={T}: NF4 quantize-on-load of gate_up+down, "
+                                f"then the experts forward from packed storage"),
+                   "E": s.E, "H": s.H, "I": s.I, "K": s.K, "T": T, "format": "nf4", "blocksize": 64},
+        "forward_ms": fwd,
+        "forward_TFLOPs": f_flops / (fwd * 1e-3) / 1e12,
+        "forward_mfma_frac": f_flops / (fwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "quantize_ms": qt,
+        "quantize_GBps": q_bytes / (qt * 1e-3) / 1e9,
+        "quantize_hbm_frac": q_bytes / (qt * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "stage_ms": avg,
+        "touched_experts": U,
+        "roofline": roof,
+    }
+
+    if not args.no_decode:
+        dec = {}
+        for Td in (1, 32):
+            xd = syn.hidden_states(Td, s.H, device=dev, layer=1)
+            idd, wd = syn.routing(Td, s.K, s.E, kind=s.routing, device=dev, layer=1)
+            od = torch.empty((Td, s.H), dtype=torch.bfloat16, device=dev)
+            wsd = torch.empty(moeq.moeq_experts_forward_workspace_bytes(Td, s.K, qg, qd),
+                              dtype=torch.uint8, device=dev)
+            reps = 50
+            evd = [new_events(torch, 5) for _ in range(reps + 5)]
+            for r in range(reps + 5):
+                moeq.moeq_experts_forward(xd, idd, wd, qg, qd, out=od, workspace=wsd,
+                                          stage_events=[h.cuda_event for h in evd[r]])
+            torch.cuda.synchronize()
+            tms = float(np.mean([e[0].elapsed_time(e[4]) for e in evd[5:]]))
+            kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evd[5:]]))
+                   for j, n in enumerate(["route", "g1_gate_up_swiglu", "g2_down", "combine"])}
+            b, fl, Ud = forward_bytes_flops(s, idd.cpu().numpy(), Td)
+            dec[f"T{Td}"] = {"tokens_per_s": Td / (tms * 1e-3), "forward_ms": tms,
+                             "packed_GBps": b / (tms * 1e-3) / 1e9,
+                             "hbm_frac": b / (tms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "touched_experts": Ud, "stage_ms": kms}
+        result["decode"] = dec
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, gu, dn, x, idx, wts, T)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -68,6 +68,7 @@ def _load():
         "moeq_dequantize": (I32, [QP, P, P]),
         "moeq_experts_forward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
         "moeq_experts_forward": (I32, [P, P, P, I32, I32, QP, QP, P, P, SZ, P]),
+        "moeq_experts_forward_timed": (I32, [P, P, P, I32, I32, QP, QP, P, P, SZ, P, P]),
         "moeq_route_workspace_bytes": (SZ, [I32, I32, I32]),
         "moeq_route_buckets": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
     }
@@ -201,8 +202,12 @@ def moeq_experts_forward_workspace_bytes(T, K, gate_up, down):
 
 
 def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=None,
-                         workspace=None, stream=None):
-    """Routed experts forward from packed storage; returns bf16 ``[T, H]``."""
+                         workspace=None, stream=None, stage_events=None):
+    """Routed experts forward from packed storage; returns bf16 ``[T, H]``.
+
+    ``stage_events``: optional sequence of 5 raw hipEvent_t handles (ints),
+    recorded at the stage boundaries (``moeq_experts_forward_timed``).
+    """
     _dev(hidden, torch.bfloat16, "hidden")
     _dev(top_k_index, torch.int32, "top_k_index")
     _dev(top_k_weights, torch.float32, "top_k_weights")
@@ -220,9 +225,15 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
     need = int(lib.moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
-    _check(lib.moeq_experts_forward(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
-                                    ctypes.byref(gu), ctypes.byref(dn), _ptr(out), _ptr(workspace),
-                                    workspace.numel(), _stream(stream)), "moeq_experts_forward")
+    args = (_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K), ctypes.byref(gu),
+            ctypes.byref(dn), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    if stage_events is None:
+        _check(lib.moeq_experts_forward(*args), "moeq_experts_forward")
+    else:
+        if len(stage_events) != 5:
+            raise ValueError("stage_events must hold 5 hipEvent_t handles")
+        arr = (ctypes.c_void_p * 5)(*[int(e) for e in stage_events])
+        _check(lib.moeq_experts_forward_timed(*args, arr), "moeq_experts_forward_timed")
     return out
 
 

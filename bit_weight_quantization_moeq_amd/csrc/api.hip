@@ -162,6 +162,13 @@ size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qwe
 moeq_status moeq_experts_forward(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T, int32_t K,
                                  const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return moeq_experts_forward_timed(x, idx, wts, T, K, gu, dn, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,
+                                       int32_t K, const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       void* const* stage_events) {
   moeq_status st = check_forward_shapes(T, K, gu, dn);
   if (st != MOEQ_OK) return st;
   if (T == 0) return MOEQ_OK;
@@ -182,7 +189,8 @@ moeq_status moeq_experts_forward(const uint16_t* x, const int32_t* idx, const fl
   a.rb = route_buffers(workspace, L);
   a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
   a.y = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.y);
-  return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream)));
+  return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream),
+                                             reinterpret_cast<hipEvent_t const*>(stage_events)));
 }
 
 size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E) {

@@ -375,10 +375,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 
 int32_t forward_tile_rows() { return kBM; }
 
-hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s) {
+hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
+  if (ev) hipEventRecord(ev[0], s);
   hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
+  if (ev) hipEventRecord(ev[1], s);
   const int mtiles = (n + kBM - 1) / kBM + a.E;  // upper bound on sum_e ceil(count_e / kBM)
   const dim3 g1(mtiles, a.I / kG1Cols), g2(mtiles, (a.H + kG2Cols - 1) / kG2Cols);
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
@@ -386,15 +388,19 @@ hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s) {
   if (a.format == MOEQ_FMT_NF4) {
     g1_kernel<MOEQ_FMT_NF4><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.rb.offsets,
                                                     a.rb.tile_start, a.rb.perm, a.h);
+    if (ev) hipEventRecord(ev[2], s);
     g2_kernel<MOEQ_FMT_NF4><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.rb.offsets,
                                                     a.rb.tile_start, a.rb.perm, a.y);
   } else {
     g1_kernel<MOEQ_FMT_INT8_ROWWISE><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s,
                                                              a.rb.offsets, a.rb.tile_start, a.rb.perm, a.h);
+    if (ev) hipEventRecord(ev[2], s);
     g2_kernel<MOEQ_FMT_INT8_ROWWISE><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s,
                                                              a.rb.offsets, a.rb.tile_start, a.rb.perm, a.y);
   }
+  if (ev) hipEventRecord(ev[3], s);
   combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.rb.slot, a.K, a.H, a.out);
+  if (ev) hipEventRecord(ev[4], s);
   return hipGetLastError();
 }
 

@@ -88,7 +88,8 @@ struct ForwardArgs {
   uint16_t* h;              // [T*K][I] bf16, expert-sorted rows
   float* y;                 // [T*K][H] fp32, expert-sorted rows
 };
-hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s);
+// events: NULL or 5 events recorded at the stage boundaries.
+hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
 int32_t forward_tile_rows();
 
 }  // namespace moeq

@@ -162,6 +162,19 @@ moeq_status moeq_experts_forward(const uint16_t *hidden_bf16, const int32_t *top
                                  void *stream);
 
 /*
+ * moeq_experts_forward with stage timing: stage_events is NULL or an array of
+ * 5 hipEvent_t (created by the caller) recorded on `stream` before routing,
+ * after routing, after the gate_up GEMM, after the down GEMM and after the
+ * combine, so the caller can time each stage with hipEventElapsedTime.
+ * Otherwise identical to moeq_experts_forward.
+ */
+moeq_status moeq_experts_forward_timed(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                       const float *top_k_weights, int32_t T, int32_t K,
+                                       const moeq_qweight *gate_up, const moeq_qweight *down,
+                                       uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
+                                       void *stream, void *const *stage_events);
+
+/*
  * The routing stage of moeq_experts_forward on its own (same kernels):
  * groups the T*K assignments a = t*K + k by expert (unsloth-zoo issue #850,
  * Suggested fix: one generic routing for every architecture).

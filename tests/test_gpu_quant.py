@@ -9,6 +9,7 @@ import moeq_synth as syn
 from oracle.bf16 import bf16_to_f32, f32_to_bf16
 from oracle.int8 import int8_dequantize_rowwise, int8_quantize_rowwise
 from oracle.nf4 import nf4_dequantize, nf4_quantize
+from moeq_synth import bf16_bits
 from tests.gpu_common import dev_bf16, host, host_bits, require_native, say
 
 pytestmark = pytest.mark.gpu
@@ -84,7 +85,7 @@ def test_nf4_edge_blocks_and_ragged_count():
     w[0, 1, 5] = -0.0
     w[1, 2, :64] *= np.float32(1e-30)                                    # absmax ~1e-32 (< 2^-90)
     w[1, 3, :64] = (rng.standard_normal(64) * 1e-38).astype(np.float32)  # bf16-subnormal range
-    w[1, 4, 64:128] *= np.float32(1e39)                                # huge values
+    w[1, 4, 64:128] *= np.float32(2.0 ** 120)                          # huge values (finite)
     w[2, 0, :64] = np.float32(0.3)                                       # constant block
     w[2, 1, 128:] = -np.float32(0.3)
     _check_nf4(f32_to_bf16(w), "edge blocks")
