@@ -91,6 +91,8 @@ moeq_status check_forward_shapes(int32_t T, int32_t K, const moeq_qweight* gu, c
   if (dn->rows != H || dn->cols != I) return MOEQ_ESHAPE;
   if (H % 64 != 0 || I % 64 != 0) return MOEQ_ESHAPE;
   if ((int64_t)T * K > kMaxAssignments) return MOEQ_ESHAPE;
+  // the GEMM kernels address rows of hidden_states with 32-bit byte offsets
+  if ((int64_t)T * H * 2 >= (int64_t(1) << 32)) return MOEQ_ESHAPE;
   return MOEQ_OK;
 }
 

@@ -6,21 +6,37 @@
 // Suggested fix: the (hidden_states, top_k_index, top_k_weights) interface).
 //
 // After the routing stage has sorted the assignments by expert:
-//   G1  grouped GEMM over tiles (expert, 128 sorted assignments, 64 columns of
-//       h): the gathered bf16 rows of x times the gate and up weight rows,
-//       dequantized tile by tile into LDS as bf16, on v_mfma_f32_32x32x16_bf16
-//       with fp32 accumulation; the epilogue pairs gate column j with up
-//       column j and writes h = bf16(silu(g) * u) in sorted order.
-//   G2  the same machinery over (expert, 128 sorted rows, 128 columns of the
-//       output): h times the dequantized down rows, scaled by the routing
-//       weight in fp32, written as fp32 y in sorted order.
+//   G1  grouped GEMM over tiles (expert, 128 sorted assignments, 128 columns of
+//       h): gathered bf16 rows of x times the gate and up weight rows, with
+//       fp32 accumulation on v_mfma_f32_32x32x16_bf16; the epilogue pairs gate
+//       column j with up column j and writes h = bf16(silu(g) * u).
+//   G2  the same machinery over (expert, 128 sorted rows, 256 output columns):
+//       h times the down rows, scaled by the routing weight in fp32 -> y.
 //   C1  out[t] = bf16(sum over k = 0..K-1, in that order, of y[slot[t*K+k]]).
 // No float atomics anywhere: every output element has one writer, so the
-// forward is bit-identical run to run.
+// forward is bit-identical run to run and independent of the batch.
 //
-// The weights are the MFMA A operand (rows of the weight on the 32 M lanes)
-// and the token rows the B operand, so each lane's accumulators hold four
-// consecutive output columns of one token row, stored as 8- or 16-byte writes.
+// Data flow inside a GEMM workgroup (4 waves):
+//   * The token rows of the tile (x rows gathered through perm, or h rows)
+//     stream through a double-buffered LDS tile, one K step ahead, shared by
+//     the 4 waves: they are the MFMA B operand.
+//   * Each wave owns its own weight rows (G1: 32 gate + the matching 32 up
+//     rows; G2: 64 down rows).  It loads their packed codes straight into
+//     registers one K step ahead and dequantizes them in registers into the
+//     MFMA A operand -- the weights never touch LDS.  The dequantized value is
+//     exactly bf16_rne(fp32(level * absmax)) / bf16_rne(fp32(q * scale)), the
+//     same bits moeq_dequantize writes.
+//   * K is permuted inside each K step (the GEMM does not care which k each
+//     MFMA lane slot holds, as long as both operands agree): lane half h of
+//     every MFMA covers one whole 64-wide NF4 block of its row, so one absmax
+//     and one 16-entry bf16 table serve the lane for the whole K step.  NF4
+//     codes become bf16 through v_perm_b32 byte lookups in that table; within
+//     each group of 8 k the order is evens-first (the order the nibbles come
+//     out of a code byte), and the token rows are written to LDS in the same
+//     order.
+//   * Work items (expert, token tile, column tile) are laid out expert-major
+//     and dealt to the 8 XCDs in contiguous ranges, so the tiles that share an
+//     expert's weights and token rows run on the same L2.
 #include "moeq_internal.h"
 
 namespace moeq {
@@ -28,143 +44,38 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;        // sorted assignment rows per tile
-constexpr int kBK = 64;         // K step (= one NF4 block)
-constexpr int kG1Cols = 64;     // h columns per G1 tile (64 gate + 64 up weight rows)
-constexpr int kG2Cols = 128;    // output columns per G2 tile
-constexpr int kWRows = 128;     // weight rows staged per K step (both kernels)
-constexpr int kLds = kBK + 8;   // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
+constexpr int kWaves = 4;
+constexpr int kBM = 256;             // sorted assignment rows per tile (at most)
+constexpr int kG1Cols = 32 * kWaves; // h columns per G1 tile (each wave: 32 gate + 32 up rows)
+constexpr int kG2Rows = 64 * kWaves; // output columns per G2 tile (each wave: 64 down rows)
+constexpr int kXcds = 8;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<MOEQ_FMT_NF4> {
+  static constexpr int kStep = 128;  // two NF4 blocks: one per MFMA lane half
+};
+template <>
+struct Fmt<MOEQ_FMT_INT8_ROWWISE> {
+  static constexpr int kStep = 64;
+};
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// ---------------------------------------------------------------------------
-// Weight staging: 128 weight rows x 64 k per step.  Thread t owns row t/2 and
-// the k half t%2 (32 elements): it fetches the packed bytes into registers
-// for the next step while the MFMAs of this step run, then dequantizes them
-// into LDS as bf16 exactly as moeq_dequantize would:
-// bf16_rne(fp32(level * absmax)) or bf16_rne(fp32(q * scale)).
-// ---------------------------------------------------------------------------
-template <int FMT>
-struct WeightStage;
-
-template <>
-struct WeightStage<MOEQ_FMT_NF4> {
-  uint4 codes;   // 32 codes (16 B)
-  float scale;   // absmax of the row's 64-block
-  bool valid;
-
-  // row: weight row index within the expert tensor (rows x cols), k0: K offset
-  __device__ __forceinline__ void fetch(const uint8_t* q, const float* s, int64_t row_global, int cols,
-                                        int k0, int half, bool ok) {
-    valid = ok;
-    if (ok) {
-      codes = *reinterpret_cast<const uint4*>(q + (row_global * cols + k0 + 32 * half) / 2);
-      scale = s[row_global * (cols / kNf4Block) + k0 / kNf4Block];
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* dst, const float* lv) const {
-    uint4 out[4];
-    if (valid) {
-      const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t o[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t byte = (w[i] >> (8 * m)) & 0xffu;
-          o[m] = pack_bf16x2(lv[byte >> 4] * scale, lv[byte & 0xfu] * scale);
-        }
-        out[i] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[i] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(dst)[i] = out[i];
-  }
-};
-
-template <>
-struct WeightStage<MOEQ_FMT_INT8_ROWWISE> {
-  uint4 q0, q1;  // 32 int8 codes
-  float scale;
-  bool valid;
-
-  __device__ __forceinline__ void fetch(const uint8_t* q, const float* s, int64_t row_global, int cols,
-                                        int k0, int half, bool ok) {
-    valid = ok;
-    if (ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(q + row_global * cols + k0 + 32 * half);
-      q0 = p[0];
-      q1 = p[1];
-      scale = s[row_global];
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* dst, const float*) const {
-    uint4 out[4];
-    if (valid) {
-      const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t o[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t d = w[2 * i + m / 2];
-          const int sh = 16 * (m & 1);
-          const float f0 = (float)(int8_t)((d >> sh) & 0xffu) * scale;
-          const float f1 = (float)(int8_t)((d >> (sh + 8)) & 0xffu) * scale;
-          o[m] = pack_bf16x2(f0, f1);
-        }
-        out[i] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[i] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(dst)[i] = out[i];
-  }
-};
-
-// Token rows: 128 rows x 64 k of bf16 per step; thread t owns row t/2, half t%2.
-struct RowStage {
-  uint4 v[4];
-  __device__ __forceinline__ void fetch(const uint16_t* rowp, int k0, int half) {
-    if (rowp) {
-      const uint4* p = reinterpret_cast<const uint4*>(rowp + k0 + 32 * half);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* dst) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<uint4*>(dst)[i] = v[i];
-  }
-};
-
-// Expert of grouped-GEMM tile `tile` (tile_start is the exclusive prefix of
-// per-expert tile counts); -1 past the last tile.
-__device__ __forceinline__ int tile_expert(const int32_t* tile_start, int E, int tile) {
-  if (tile >= tile_start[E]) return -1;
-  int lo = 0, hi = E - 1;  // largest e with tile_start[e] <= tile
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base) {
-  return *reinterpret_cast<const bf16x8*>(base);
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -172,87 +83,339 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------
-// G1: h[p][j] = bf16(silu(gate_j . x) * (up_j . x)) for the tile's rows p.
-// Wave w: h columns 32*(w&1) .. +32 (gate and up), rows 64*(w>>1) .. +64.
+// NF4 dequantization in registers.
 // ---------------------------------------------------------------------------
+// Byte tables of the 16 dequantized values of one (row, 64-block):
+// T_i = bf16_rne(fp32(level_i * absmax)); lo[q] holds the low bytes of
+// T_{4q..4q+3}, hi[q] the high bytes.
+struct Nf4Table {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ Nf4Table nf4_table(float a) {
+  uint32_t p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    p[j] = pack_bf16x2(__uint_as_float(kNf4LevelBits[2 * j]) * a, __uint_as_float(kNf4LevelBits[2 * j + 1]) * a);
+  Nf4Table t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// One dword of packed codes (8 consecutive k; byte m holds k = 2m in its high
+// nibble and k = 2m + 1 in its low nibble) -> the A operand [k0 .. k7].
+__device__ __forceinline__ bf16x8 nf4_frag(const Nf4Table& t, uint32_t w) {
+  // v_perm selectors 8..11 replicate the sign bit of pool bytes 1, 3, 5, 7:
+  // with pool {w, w << 8} they give 0xff exactly where a byte of w has bit 7
+  // set, i.e. where the high-nibble code is >= 8; shifting w by 4 first does
+  // the same for the low-nibble codes.
+  const uint32_t me = perm(w, w << 8, 0x0B090A08u);
+  const uint32_t mo = perm(w << 4, w << 12, 0x0B090A08u);
+  const uint32_t se = (w >> 4) & 0x07070707u, so = w & 0x07070707u;
+  // low / high bytes of the values of the even-k codes (k0 k2 k4 k6) and of the
+  // odd-k codes (k1 k3 k5 k7)
+  const uint32_t le = (me & perm(t.lo[3], t.lo[2], se)) | (~me & perm(t.lo[1], t.lo[0], se));
+  const uint32_t he = (me & perm(t.hi[3], t.hi[2], se)) | (~me & perm(t.hi[1], t.hi[0], se));
+  const uint32_t lo = (mo & perm(t.lo[3], t.lo[2], so)) | (~mo & perm(t.lo[1], t.lo[0], so));
+  const uint32_t ho = (mo & perm(t.hi[3], t.hi[2], so)) | (~mo & perm(t.hi[1], t.hi[0], so));
+  // interleave back to k order: low bytes of k0..k3, high bytes of k0..k3, ...
+  const uint32_t l03 = perm(lo, le, 0x05010400u), h03 = perm(ho, he, 0x05010400u);
+  const uint32_t l47 = perm(lo, le, 0x07030602u), h47 = perm(ho, he, 0x07030602u);
+  return as_bf16x8(perm(h03, l03, 0x05010400u), perm(h03, l03, 0x07030602u), perm(h47, l47, 0x05010400u),
+                   perm(h47, l47, 0x07030602u));
+}
+
+// ---------------------------------------------------------------------------
+// int8 dequantization in registers: bf16_rne(fp32(q * s)).  q + 128 is the
+// unsigned byte of q ^ 0x80, and fma(u, s, -128 s) rounds the exact q * s
+// once, exactly like the plain product.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 i8_frag(uint32_t w0, uint32_t w1, float s, float ns128) {
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = __builtin_fmaf((float)((u0 >> (8 * j)) & 0xffu), s, ns128);
+    f[4 + j] = __builtin_fmaf((float)((u1 >> (8 * j)) & 0xffu), s, ns128);
+  }
+  return as_bf16x8(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7]));
+}
+
+// One weight row's share of a K step for one lane: the packed codes of the
+// lane's half of the step and the row scale (NF4: absmax of the 64-block).
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict__ x, int32_t K, int32_t E,
-                                                     int32_t H, int32_t I, const uint8_t* __restrict__ wq,
-                                                     const float* __restrict__ ws,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const int32_t* __restrict__ tile_start,
-                                                     const int32_t* __restrict__ perm,
-                                                     uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[kWRows * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[kBM * kLds];
-  __shared__ float lv[16];
+struct RowCodes {
+  uint4 c0, c1;
+  float scale;
 
-  const int e = tile_expert(tile_start, E, blockIdx.x);
-  if (e < 0) return;
-  const int row0 = offsets[e] + (blockIdx.x - tile_start[e]) * kBM;
-  const int nrows = min(kBM, offsets[e + 1] - row0);
-  const int j0 = blockIdx.y * kG1Cols;
-
-  if (threadIdx.x < 16) lv[threadIdx.x] = __uint_as_float(kNf4LevelBits[threadIdx.x]);
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // staging roles
-  const int srow = t >> 1, half = t & 1;
-  const int64_t wrow = (int64_t)e * 2 * I + (srow < kG1Cols ? j0 + srow : I + j0 + (srow - kG1Cols));
-  const uint16_t* xrow = (srow < nrows) ? x + (int64_t)(perm[row0 + srow] / K) * H : nullptr;
-
-  WeightStage<FMT> wst;
-  RowStage xst;
-  wst.fetch(wq, ws, wrow, H, 0, half, true);
-  xst.fetch(xrow, 0, half);
-
-  f32x16 acc[2][2];  // [gate/up][token block]
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[g][b] = (f32x16){};
-
-  const int wj = wave & 1, wi = wave >> 1;
-  const int l32 = lane & 31, khi = 8 * (lane >> 5);
-  const uint16_t* aG = sW + (32 * wj + l32) * kLds + khi;
-  const uint16_t* aU = sW + (kG1Cols + 32 * wj + l32) * kLds + khi;
-  const uint16_t* b0 = sX + (64 * wi + l32) * kLds + khi;
-  const uint16_t* b1 = sX + (64 * wi + 32 + l32) * kLds + khi;
-
-  const int nks = H / kBK;
-  for (int ks = 0; ks < nks; ++ks) {
-    __syncthreads();
-    wst.store(sW + srow * kLds + 32 * half, lv);
-    xst.store(sX + srow * kLds + 32 * half);
-    __syncthreads();
-    if (ks + 1 < nks) {
-      wst.fetch(wq, ws, wrow, H, (ks + 1) * kBK, half, true);
-      xst.fetch(xrow, (ks + 1) * kBK, half);
-    }
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const bf16x8 ag = lds_frag(aG + 16 * s), au = lds_frag(aU + 16 * s);
-      const bf16x8 x0 = lds_frag(b0 + 16 * s), x1 = lds_frag(b1 + 16 * s);
-      acc[0][0] = mfma(ag, x0, acc[0][0]);
-      acc[0][1] = mfma(ag, x1, acc[0][1]);
-      acc[1][0] = mfma(au, x0, acc[1][0]);
-      acc[1][1] = mfma(au, x1, acc[1][1]);
+  // row_base: codes of the row; srow: scale pointer of the row (NF4: its
+  // first block); k0: K step start; hh: lane half; K: row length; ok: row valid.
+  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K,
+                                        bool ok) {
+    constexpr int half = Fmt<FMT>::kStep / 2;
+    const int kk = k0 + half * hh;
+    if (ok && kk < K) {
+      const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kk / 2 : kk));
+      c0 = p[0];
+      c1 = p[1];
+      scale = (FMT == MOEQ_FMT_NF4) ? srow[kk / kNf4Block] : srow[0];
+    } else {
+      c0 = make_uint4(0, 0, 0, 0);
+      c1 = make_uint4(0, 0, 0, 0);
+      scale = 0.0f;  // NF4: all-zero table; int8: zero scale -> the A operand is exactly zero
     }
   }
+  __device__ __forceinline__ uint32_t word(int i) const {
+    const uint4& c = (i < 4) ? c0 : c1;
+    const int j = i & 3;
+    return j == 0 ? c.x : (j == 1 ? c.y : (j == 2 ? c.z : c.w));
+  }
+};
 
-  // epilogue: lane holds, per token block b and register quad q, the four
-  // h columns 8q + 4*(lane/32) + 0..3 of token row l32.
+template <int FMT>
+struct Dequant;
+
+template <>
+struct Dequant<MOEQ_FMT_NF4> {
+  Nf4Table t;
+  __device__ __forceinline__ void prepare(const RowCodes<MOEQ_FMT_NF4>& r) { t = nf4_table(r.scale); }
+  // MFMA step s (0..7) of the K step: codes word s = 8 consecutive k of the block
+  __device__ __forceinline__ bf16x8 frag(const RowCodes<MOEQ_FMT_NF4>& r, int s) const {
+    return nf4_frag(t, r.word(s));
+  }
+};
+
+template <>
+struct Dequant<MOEQ_FMT_INT8_ROWWISE> {
+  float s, ns128;
+  __device__ __forceinline__ void prepare(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r) {
+    s = r.scale;
+    ns128 = -128.0f * r.scale;
+  }
+  // MFMA step s (0..3): 8 consecutive int8 codes = words 2s, 2s+1
+  __device__ __forceinline__ bf16x8 frag(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r, int s_) const {
+    return i8_frag(r.word(2 * s_), r.word(2 * s_ + 1), s, ns128);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Work items: expert-major (expert, column tile, token tile), dealt to the
+// XCDs in contiguous ranges.  tile_start = exclusive prefix of per-expert
+// token-tile counts.
+// ---------------------------------------------------------------------------
+// Rows [*row0, *row0 + *nrows) of tile mt of expert e: the expert's rows
+// split into tile_start[e+1] - tile_start[e] near-equal tiles (at most kBM
+// rows each, since the count is ceil(rows / kBM)).
+__device__ __forceinline__ void tile_rows(const int32_t* offsets, const int32_t* tile_start, int e, int mt,
+                                          int* row0, int* nrows) {
+  const int c = offsets[e + 1] - offsets[e];
+  const int nt = tile_start[e + 1] - tile_start[e];
+  const int lo = (int)((int64_t)mt * c / nt), hi = (int)((int64_t)(mt + 1) * c / nt);
+  *row0 = offsets[e] + lo;
+  *nrows = hi - lo;
+}
+
+__device__ __forceinline__ bool decode_work(const int32_t* tile_start, int E, int ncol, int& e, int& mt,
+                                            int& ct) {
+  const int total = tile_start[E] * ncol;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int w = (blockIdx.x % kXcds) * per + slot;
+  if (slot >= per || w >= total) return false;
+  int lo = 0, hi = E - 1;  // largest e with tile_start[e] * ncol <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] * ncol <= w) lo = mid; else hi = mid - 1;
+  }
+  e = lo;
+  const int r = w - tile_start[e] * ncol;
+  const int nt = tile_start[e + 1] - tile_start[e];
+  ct = r / nt;
+  mt = r - ct * nt;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM core shared by G1 and G2: NB token blocks of 32 rows (the tile's
+// 32*NB sorted rows, MFMA B operand, from LDS) times two 32-row weight
+// blocks per wave (MFMA A operand, dequantized in registers), accumulated
+// over K.
+//
+// Token rows go global -> LDS directly (global_load_lds_dwordx4: lane l of a
+// wave lands 16 B at the wave's LDS base + 16 l), one K step ahead.  One
+// instruction of a wave moves whole row segments (4 rows x 256 B for NF4,
+// 8 rows x 128 B for int8), so every cache line it touches is used in full.
+// The LDS tile is row-major with the 16-B slots of a row XOR-swizzled by the
+// row, so the fragment reads (32 consecutive rows, one k chunk) hit distinct
+// banks.  The swizzle is the same for every row a lane stages, so a lane's
+// source offset within a row is one constant.  Rows past the tile stage a
+// valid row (their results are never stored); k past the end meets zero
+// weights.
+// ---------------------------------------------------------------------------
+template <int FMT, int NB>
+struct Core {
+  static constexpr int kStep = Fmt<FMT>::kStep;
+  static constexpr int kRows = 32 * NB;
+  static constexpr int kCpr = kStep / 8;                  // 16-B chunks per row per step
+  static constexpr int kRpi = 64 / kCpr;                  // rows per wave instruction
+  static constexpr int kInstr = kRows / (kWaves * kRpi);  // staging instructions per wave per step
+  static constexpr int kBufBytes = kRows * kCpr * 16;
+
+  // slot swizzle of row r: conflict-free for 16 consecutive rows
+  __device__ __forceinline__ static int swz(int r) { return kCpr == 16 ? (r & 15) : ((r >> 1) & 7); }
+  // the tile row staged by lane l of wave w in instruction i
+  __device__ __forceinline__ static int staged_row(int w, int l, int i) { return kRpi * (kWaves * i + w) + l / kCpr; }
+
+  // sX: two LDS buffers; tbase + roff[i]: byte address of the row staged in
+  // instruction i; K: reduction length; (q0, s0) / (q1, s1): this lane's two
+  // weight rows.
+  __device__ __forceinline__ static void run(char* sX, int buf_bytes, const char* tbase, const uint32_t (&roff)[kInstr],
+                                             int K, const uint8_t* q0, const float* s0, const uint8_t* q1,
+                                             const float* s1, bool wave_on, f32x16 (&acc0)[NB],
+                                             f32x16 (&acc1)[NB]) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    // source chunk of this lane within its row (the same for every instruction)
+    const int chunk = (lane % kCpr) ^ swz(staged_row(wave, lane, 0));
+    char* stage0 = sX + staged_row(wave, 0, 0) * kCpr * 16;
+
+    auto stage = [&](int k0, int buf) {
+      int kk = k0 + 8 * chunk;
+      kk = kk < K ? kk : 0;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = 64 * wi + 32 * b + l32;
+      for (int i = 0; i < kInstr; ++i) {
+        __builtin_amdgcn_global_load_lds(tbase + roff[i] + 2 * kk,
+                                         stage0 + buf * buf_bytes + i * kWaves * kRpi * kCpr * 16, 16, 0, 0);
+      }
+    };
+
+    RowCodes<FMT> c0, c1;
+    stage(0, 0);
+    c0.fetch(q0, s0, 0, hh, K, wave_on);
+    c1.fetch(q1, s1, 0, hh, K, wave_on);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // B fragment of token block b at MFMA step s: row 32b + l32, chunk
+    // (kCpr/2)*hh + s, stored at slot chunk ^ swz(row) (swz(row) = swz(l32)).
+    const int rsw = swz(l32);
+    // Straight-line body (no branches around the MFMAs, so the accumulators
+    // stay put): a wave with no weight rows multiplies zeros, and the last
+    // step prefetches a harmless extra step (zero codes, an in-range row).
+    const int nks = (K + kStep - 1) / kStep;
+    for (int ks = 0; ks < nks; ++ks) {
+      const int buf = ks & 1;
+      RowCodes<FMT> n0, n1;
+      stage((ks + 1) * kStep, buf ^ 1);
+      n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
+      n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+      Dequant<FMT> d0, d1;
+      d0.prepare(c0);
+      d1.prepare(c1);
+      const char* xb = sX + buf * buf_bytes + l32 * kCpr * 16;
+      auto bfrag = [&](int s_, int b) {
+        const int slot = ((kCpr / 2) * hh + s_) ^ rsw;
+        return *reinterpret_cast<const bf16x8*>(xb + (32 * b * kCpr + slot) * 16);
+      };
+      // Software pipeline over the MFMA steps of the K step: while step s's
+      // 2*NB MFMAs run, the B fragments of step s+1 are read from LDS and its
+      // A fragments are dequantized.
+      constexpr int kS = kStep / 16;
+      bf16x8 a0 = d0.frag(c0, 0), a1 = d1.frag(c1, 0);
+      bf16x8 xf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xf[b] = bfrag(0, b);
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        bf16x8 xn[NB], a0n, a1n;
+        if (s + 1 < kS) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) xn[b] = bfrag(s + 1, b);
+          a0n = d0.frag(c0, s + 1);
+          a1n = d1.frag(c1, s + 1);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc0[b] = mfma(a0, xf[b], acc0[b]);
+          acc1[b] = mfma(a1, xf[b], acc1[b]);
+        }
+        if (s + 1 < kS) {
+          // interleave: the next B-fragment reads between the first MFMAs,
+          // then the next A-fragment dequantization between the rest
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          }
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 64 / NB, 0);  // VALU
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xf[b] = xn[b];
+        a0 = a0n;
+        a1 = a1n;
+      }
+      c0 = n0;
+      c1 = n1;
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's LDS-bound loads have landed
+      __syncthreads();
+    }
+  }
+};
+
+template <int FMT>
+struct Lds {
+  static constexpr int kBuf = Core<FMT, kBM / 32>::kBufBytes;  // bytes per buffer (largest tile)
+};
+
+// ---------------------------------------------------------------------------
+// G1: h[p][j] = bf16(silu(gate_j . x) * (up_j . x)) for the tile's rows p.
+// Wave w: h columns jcol = j0 + 32w .. +32 (gate rows jcol.., up rows I + jcol..).
+// ---------------------------------------------------------------------------
+template <int FMT, int NB>
+__device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32_t* prow, int K, int H, int I,
+                                        int jcol, bool wave_on, const uint8_t* gq, const float* gs,
+                                        const uint8_t* uq, const float* us, int row0, int nrows,
+                                        uint16_t* __restrict__ h) {
+  using C = Core<FMT, NB>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t roff[C::kInstr];  // byte offset of each staged x row (token perm[p] / K)
+#pragma unroll
+  for (int i = 0; i < C::kInstr; ++i) {
+    const int r = C::staged_row(wave, lane, i);
+    roff[i] = (uint32_t)(prow[r < nrows ? r : 0] / K) * (uint32_t)H * 2u;
+  }
+  f32x16 accG[NB], accU[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    accG[b] = (f32x16){};
+    accU[b] = (f32x16){};
+  }
+  C::run(sX, Lds<FMT>::kBuf, reinterpret_cast<const char*>(x), roff, H, gq, gs, uq, us, wave_on, accG, accU);
+  if (!wave_on) return;
+  // lane holds, per token block b and register quad q, the four h columns
+  // jcol + 8q + 4*hh + 0..3 of token row 32b + l32.
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = 32 * b + l32;
     if (r >= nrows) continue;
-    uint16_t* hp = h + (int64_t)(row0 + r) * I + j0 + 32 * wj + 4 * (lane >> 5);
+    uint16_t* hp = h + (int64_t)(row0 + r) * I + jcol + 4 * hh;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float g = acc[0][b][4 * q + i], u = acc[1][b][4 * q + i];
+        const float g = accG[b][4 * q + i], u = accU[b][4 * q + i];
         v[i] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
       }
       *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -260,95 +423,121 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict__ x, int32_t K, int32_t E,
+                                                     int32_t H, int32_t I, const uint8_t* __restrict__ wq,
+                                                     const float* __restrict__ ws,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ tile_start,
+                                                     const int32_t* __restrict__ perm_idx,
+                                                     uint16_t* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) char sX[2 * Lds<FMT>::kBuf];
+
+  int e, mt, ct;
+  if (!decode_work(tile_start, E, (I + kG1Cols - 1) / kG1Cols, e, mt, ct)) return;
+  int row0, nrows;
+  tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
+  const int wave = threadIdx.x >> 6, l32 = threadIdx.x & 31;
+
+  const int jcol = ct * kG1Cols + 32 * wave;
+  const bool wave_on = jcol < I;  // I % 32 == 0
+  const int64_t grow = (int64_t)e * 2 * I + jcol + l32;
+  const int64_t urow = grow + I;
+  const int cpr = (FMT == MOEQ_FMT_NF4) ? H / 2 : H;  // code bytes per row
+  const int spr = (FMT == MOEQ_FMT_NF4) ? H / kNf4Block : 1;
+
+  const uint8_t* gq = wq + grow * cpr;
+  const uint8_t* uq = wq + urow * cpr;
+  const float* gs = ws + grow * spr;
+  const float* us = ws + urow * spr;
+  const int32_t* prow = perm_idx + row0;
+  if (nrows > 192)
+    g1_tile<FMT, 8>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+  else if (nrows > 128)
+    g1_tile<FMT, 6>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+  else if (nrows > 64)
+    g1_tile<FMT, 4>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+  else
+    g1_tile<FMT, 2>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+}
+
 // ---------------------------------------------------------------------------
-// G2: y[p][n] = w_p * (down_n . h_p) in fp32 for the tile's rows p.
-// Wave w: output columns 64*(w&1) .. +64, rows 64*(w>>1) .. +64.
+// G2: y[p][n] = w_p * (down_n . h_p) in fp32.  Wave w: output columns
+// ncol = n0 + 64w .. +64 (two 32-row MFMA blocks).
 // ---------------------------------------------------------------------------
+template <int FMT, int NB>
+__device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_t* h, int H, int I, int ncol,
+                                        bool on, const uint8_t* q0, const float* s0, const uint8_t* q1,
+                                        const float* s1, int row0, int nrows, float* __restrict__ y) {
+  using C = Core<FMT, NB>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t roff[C::kInstr];  // byte offset of each staged h row (relative to the tile's first row)
+#pragma unroll
+  for (int i = 0; i < C::kInstr; ++i) {
+    const int r = C::staged_row(wave, lane, i);
+    roff[i] = (uint32_t)(r < nrows ? r : 0) * (uint32_t)I * 2u;
+  }
+  f32x16 acc0[NB], acc1[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    acc0[b] = (f32x16){};
+    acc1[b] = (f32x16){};
+  }
+  C::run(sX, Lds<FMT>::kBuf, reinterpret_cast<const char*>(h + (int64_t)row0 * I), roff, I, q0, s0, q1, s1, on,
+         acc0, acc1);
+  if (!on) return;
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = 32 * b + l32;
+    if (r >= nrows) continue;
+    const float wr = sw[r];
+    float* yp = y + (int64_t)(row0 + r) * H + ncol + 4 * hh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<float4*>(yp + 8 * q) =
+          make_float4(acc0[b][4 * q] * wr, acc0[b][4 * q + 1] * wr, acc0[b][4 * q + 2] * wr, acc0[b][4 * q + 3] * wr);
+      *reinterpret_cast<float4*>(yp + 32 + 8 * q) =
+          make_float4(acc1[b][4 * q] * wr, acc1[b][4 * q + 1] * wr, acc1[b][4 * q + 2] * wr, acc1[b][4 * q + 3] * wr);
+    }
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict__ h, const float* __restrict__ wts,
                                                      int32_t E, int32_t H, int32_t I,
                                                      const uint8_t* __restrict__ wq, const float* __restrict__ ws,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
-                                                     const int32_t* __restrict__ perm, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[kWRows * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[kBM * kLds];
-  __shared__ float lv[16];
+                                                     const int32_t* __restrict__ perm_idx, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) char sX[2 * Lds<FMT>::kBuf];
   __shared__ float sw[kBM];
 
-  const int e = tile_expert(tile_start, E, blockIdx.x);
-  if (e < 0) return;
-  const int row0 = offsets[e] + (blockIdx.x - tile_start[e]) * kBM;
-  const int nrows = min(kBM, offsets[e + 1] - row0);
-  const int n0 = blockIdx.y * kG2Cols;
+  int e, mt, ct;
+  if (!decode_work(tile_start, E, (H + kG2Rows - 1) / kG2Rows, e, mt, ct)) return;
+  int row0, nrows;
+  tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
+  const int t = threadIdx.x, wave = t >> 6, l32 = t & 31;
+  if (t < kBM) sw[t] = (t < nrows) ? wts[perm_idx[row0 + t]] : 0.0f;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t < 16) lv[t] = __uint_as_float(kNf4LevelBits[t]);
-  if (t < kBM) sw[t] = (t < nrows) ? wts[perm[row0 + t]] : 0.0f;
+  const int ncol = ct * kG2Rows + 64 * wave;  // H % 64 == 0: a wave is all in or all out
+  const bool on = ncol < H;
+  const int64_t r0 = (int64_t)e * H + ncol + l32, r1 = r0 + 32;
+  const int cpr = (FMT == MOEQ_FMT_NF4) ? I / 2 : I;
+  const int spr = (FMT == MOEQ_FMT_NF4) ? I / kNf4Block : 1;
 
-  const int srow = t >> 1, half = t & 1;
-  const bool wok = (n0 + srow) < H;
-  const int64_t wrow = (int64_t)e * H + (wok ? n0 + srow : 0);
-  const uint16_t* hrow = (srow < nrows) ? h + (int64_t)(row0 + srow) * I : nullptr;
-
-  WeightStage<FMT> wst;
-  RowStage hst;
-  wst.fetch(wq, ws, wrow, I, 0, half, wok);
-  hst.fetch(hrow, 0, half);
-
-  f32x16 acc[2][2];  // [column block][token block]
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[g][b] = (f32x16){};
-
-  const int wn = wave & 1, wi = wave >> 1;
-  const int l32 = lane & 31, khi = 8 * (lane >> 5);
-  const uint16_t* a0 = sW + (64 * wn + l32) * kLds + khi;
-  const uint16_t* a1 = sW + (64 * wn + 32 + l32) * kLds + khi;
-  const uint16_t* b0 = sX + (64 * wi + l32) * kLds + khi;
-  const uint16_t* b1 = sX + (64 * wi + 32 + l32) * kLds + khi;
-
-  const int nks = I / kBK;
-  for (int ks = 0; ks < nks; ++ks) {
-    __syncthreads();
-    wst.store(sW + srow * kLds + 32 * half, lv);
-    hst.store(sX + srow * kLds + 32 * half);
-    __syncthreads();
-    if (ks + 1 < nks) {
-      wst.fetch(wq, ws, wrow, I, (ks + 1) * kBK, half, wok);
-      hst.fetch(hrow, (ks + 1) * kBK, half);
-    }
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const bf16x8 w0 = lds_frag(a0 + 16 * s), w1 = lds_frag(a1 + 16 * s);
-      const bf16x8 x0 = lds_frag(b0 + 16 * s), x1 = lds_frag(b1 + 16 * s);
-      acc[0][0] = mfma(w0, x0, acc[0][0]);
-      acc[0][1] = mfma(w0, x1, acc[0][1]);
-      acc[1][0] = mfma(w1, x0, acc[1][0]);
-      acc[1][1] = mfma(w1, x1, acc[1][1]);
-    }
-  }
-
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int r = 64 * wi + 32 * b + l32;
-    if (r >= nrows) continue;
-    const float wr = sw[r];
-    float* yp = y + (int64_t)(row0 + r) * H;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 64 * wn + 32 * c + 8 * q + 4 * (lane >> 5);
-        if (n < H) {
-          *reinterpret_cast<float4*>(yp + n) =
-              make_float4(acc[c][b][4 * q] * wr, acc[c][b][4 * q + 1] * wr, acc[c][b][4 * q + 2] * wr,
-                          acc[c][b][4 * q + 3] * wr);
-        }
-      }
-    }
-  }
+  const uint8_t* q0 = wq + r0 * cpr;
+  const uint8_t* q1 = wq + r1 * cpr;
+  const float* s0 = ws + r0 * spr;
+  const float* s1 = ws + r1 * spr;
+  if (nrows > 192)
+    g2_tile<FMT, 8>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+  else if (nrows > 128)
+    g2_tile<FMT, 6>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+  else if (nrows > 64)
+    g2_tile<FMT, 4>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+  else
+    g2_tile<FMT, 2>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,6 +560,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
 }  // namespace
 
 int32_t forward_tile_rows() { return kBM; }
@@ -381,8 +572,10 @@ hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_
   hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[1], s);
-  const int mtiles = (n + kBM - 1) / kBM + a.E;  // upper bound on sum_e ceil(count_e / kBM)
-  const dim3 g1(mtiles, a.I / kG1Cols), g2(mtiles, (a.H + kG2Cols - 1) / kG2Cols);
+  // upper bound on the number of token tiles: sum_e ceil(count_e / kBM)
+  const int mtiles = (n + kBM - 1) / kBM + a.E;
+  const int g1 = round_up(mtiles * ((a.I + kG1Cols - 1) / kG1Cols), kXcds);
+  const int g2 = round_up(mtiles * ((a.H + kG2Rows - 1) / kG2Rows), kXcds);
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   if (a.format == MOEQ_FMT_NF4) {

@@ -153,7 +153,8 @@ size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qwe
  *                 moeq_experts_forward_workspace_bytes(T, K, gate_up, down).
  * Weights are dequantized tile by tile inside the kernels (bf16 operands,
  * fp32 accumulation); no dequantized tensor is materialised.  T == 0 is a
- * valid no-op.  H and I must be multiples of 64 (MOEQ_ESHAPE otherwise).
+ * valid no-op.  MOEQ_ESHAPE unless H and I are multiples of 64, T*K <= 2^24
+ * and hidden_states is smaller than 4 GiB.
  */
 moeq_status moeq_experts_forward(const uint16_t *hidden_bf16, const int32_t *top_k_index,
                                  const float *top_k_weights, int32_t T, int32_t K,
