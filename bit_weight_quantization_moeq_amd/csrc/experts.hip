@@ -53,6 +53,12 @@ constexpr int kG1Cols = 32 * kWaves; // h columns per G1 tile (each wave: 32 gat
 constexpr int kG2Rows = 64 * kWaves; // output columns per G2 tile (each wave: 64 down rows)
 constexpr int kXcds = 8;
 
+// s_waitcnt immediate that waits until at most N vector-memory loads are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+constexpr int kVmcntWait = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+
 template <int FMT>
 struct Fmt;
 template <>
@@ -153,22 +159,25 @@ struct RowCodes {
   uint4 c0, c1;
   float scale;
 
-  // row_base: codes of the row; srow: scale pointer of the row (NF4: its
-  // first block); k0: K step start; hh: lane half; K: row length; ok: row valid.
+  // Exactly three vector loads per call (the K-step pipeline counts on it):
+  // row_base: codes of the row (always a valid row); srow: scale pointer of
+  // the row (NF4: its first block); k0: K step start; hh: lane half; K: row
+  // length; ok: the row is real.  Outside the row or the K range the loads
+  // read the row start and the result is replaced by zeros.
+  static constexpr int kLoads = 3;
   __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K,
                                         bool ok) {
     constexpr int half = Fmt<FMT>::kStep / 2;
     const int kk = k0 + half * hh;
-    if (ok && kk < K) {
-      const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kk / 2 : kk));
-      c0 = p[0];
-      c1 = p[1];
-      scale = (FMT == MOEQ_FMT_NF4) ? srow[kk / kNf4Block] : srow[0];
-    } else {
-      c0 = make_uint4(0, 0, 0, 0);
-      c1 = make_uint4(0, 0, 0, 0);
-      scale = 0.0f;  // NF4: all-zero table; int8: zero scale -> the A operand is exactly zero
-    }
+    const bool in = ok && kk < K;
+    const int kc = in ? kk : 0;
+    const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kc / 2 : kc));
+    const uint4 a = p[0], b = p[1];
+    const float sc = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : srow[0];
+    // NF4: zero absmax -> all-zero table; int8: zero scale -> the A operand is exactly zero
+    c0 = in ? a : make_uint4(0, 0, 0, 0);
+    c1 = in ? b : make_uint4(0, 0, 0, 0);
+    scale = in ? sc : 0.0f;
   }
   __device__ __forceinline__ uint32_t word(int i) const {
     const uint4& c = (i < 4) ? c0 : c1;
@@ -259,6 +268,9 @@ __device__ __forceinline__ bool decode_work(const int32_t* tile_start, int E, in
 // ---------------------------------------------------------------------------
 template <int FMT, int NB>
 struct Core {
+  // LDS token buffers: three (token DMAs two K steps ahead) when they fit in
+  // LDS next to the largest tile's two, else two (one step ahead).
+  static constexpr int kNbuf = NB <= 6 ? 3 : 2;
   static constexpr int kStep = Fmt<FMT>::kStep;
   static constexpr int kRows = 32 * NB;
   static constexpr int kCpr = kStep / 8;                  // 16-B chunks per row per step
@@ -271,7 +283,7 @@ struct Core {
   // the tile row staged by lane l of wave w in instruction i
   __device__ __forceinline__ static int staged_row(int w, int l, int i) { return kRpi * (kWaves * i + w) + l / kCpr; }
 
-  // sX: two LDS buffers; tbase + roff[i]: byte address of the row staged in
+  // sX: kNbuf LDS buffers of buf_bytes; tbase + roff[i]: byte address of the row staged in
   // instruction i; K: reduction length; (q0, s0) / (q1, s1): this lane's two
   // weight rows.
   __device__ __forceinline__ static void run(char* sX, int buf_bytes, const char* tbase, const uint32_t (&roff)[kInstr],
@@ -294,26 +306,29 @@ struct Core {
       }
     };
 
-    RowCodes<FMT> c0, c1;
-    stage(0, 0);
-    c0.fetch(q0, s0, 0, hh, K, wave_on);
-    c1.fetch(q1, s1, 0, hh, K, wave_on);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
     // B fragment of token block b at MFMA step s: row 32b + l32, chunk
     // (kCpr/2)*hh + s, stored at slot chunk ^ swz(row) (swz(row) = swz(l32)).
     const int rsw = swz(l32);
-    // Straight-line body (no branches around the MFMAs, so the accumulators
-    // stay put): a wave with no weight rows multiplies zeros, and the last
-    // step prefetches a harmless extra step (zero codes, an in-range row).
-    const int nks = (K + kStep - 1) / kStep;
-    for (int ks = 0; ks < nks; ++ks) {
-      const int buf = ks & 1;
-      RowCodes<FMT> n0, n1;
-      stage((ks + 1) * kStep, buf ^ 1);
-      n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
-      n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+
+    // One K step: start the next step's token DMAs and code loads, run this
+    // step's MFMAs from LDS buffer ks & 1 and the codes in (c0, c1).  A straight
+    // line (no branches around the MFMAs, so the accumulators stay put): a
+    // wave with no weight rows multiplies zeros, and the last step prefetches
+    // a harmless extra step (zero codes, an in-range row).
+    auto kstep = [&](int ks, const RowCodes<FMT>& c0, const RowCodes<FMT>& c1, RowCodes<FMT>& n0,
+                     RowCodes<FMT>& n1) {
+      const int buf = ks % kNbuf;
+      if (kNbuf == 2) {
+        stage((ks + 1) * kStep, (ks + 1) % kNbuf);
+        __builtin_amdgcn_sched_barrier(0);  // the code loads below must issue after the DMAs
+        n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
+        n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+      } else {
+        n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
+        n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+        __builtin_amdgcn_sched_barrier(0);  // the DMAs below must issue after the code loads
+        stage((ks + 2) * kStep, (ks + 2) % kNbuf);
+      }
       Dequant<FMT> d0, d1;
       d0.prepare(c0);
       d1.prepare(c1);
@@ -364,17 +379,47 @@ struct Core {
         a0 = a0n;
         a1 = a1n;
       }
-      c0 = n0;
-      c1 = n1;
-      __builtin_amdgcn_s_waitcnt(0);  // this thread's LDS-bound loads have landed
-      __syncthreads();
+      // Vector loads complete in order: once at most the loads issued in this
+      // step are outstanding (2*kLoads code loads, plus with three buffers
+      // the DMAs two steps ahead), this thread's DMAs for step ks + 1 have
+      // landed in LDS; the rest keep flying across the barrier.  No release
+      // fence is needed: every LDS read of this step has been consumed by an
+      // MFMA above; the acquire fence keeps the next step's LDS reads below
+      // the barrier.
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * RowCodes<FMT>::kLoads + (kNbuf == 3 ? kInstr : 0)>);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    // two register sets for the codes, used in turn (no copies between steps)
+    RowCodes<FMT> ca0, ca1, cb0, cb1;
+    stage(0, 0);
+    ca0.fetch(q0, s0, 0, hh, K, wave_on);
+    ca1.fetch(q1, s1, 0, hh, K, wave_on);
+    if (kNbuf == 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(kStep, 1);
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<kInstr>);  // step 0 landed; step 1 may still fly
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
     }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const int nks = (K + kStep - 1) / kStep;
+    int ks = 0;
+    for (; ks + 1 < nks; ks += 2) {
+      kstep(ks, ca0, ca1, cb0, cb1);
+      kstep(ks + 1, cb0, cb1, ca0, ca1);
+    }
+    if (ks < nks) kstep(ks, ca0, ca1, cb0, cb1);
   }
 };
 
 template <int FMT>
 struct Lds {
-  static constexpr int kBuf = Core<FMT, kBM / 32>::kBufBytes;  // bytes per buffer (largest tile)
+  // bytes per buffer (largest tile), and the LDS all paths fit in
+  static constexpr int kBuf = Core<FMT, kBM / 32>::kBufBytes;
+  static constexpr int kTotal = 2 * kBuf > 3 * Core<FMT, 6>::kBufBytes ? 2 * kBuf : 3 * Core<FMT, 6>::kBufBytes;
 };
 
 // ---------------------------------------------------------------------------
@@ -400,7 +445,7 @@ __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32
     accG[b] = (f32x16){};
     accU[b] = (f32x16){};
   }
-  C::run(sX, Lds<FMT>::kBuf, reinterpret_cast<const char*>(x), roff, H, gq, gs, uq, us, wave_on, accG, accU);
+  C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(x), roff, H, gq, gs, uq, us, wave_on, accG, accU);
   if (!wave_on) return;
   // lane holds, per token block b and register quad q, the four h columns
   // jcol + 8q + 4*hh + 0..3 of token row 32b + l32.
@@ -431,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx,
                                                      uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) char sX[2 * Lds<FMT>::kBuf];
+  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
 
   int e, mt, ct;
   if (!decode_work(tile_start, E, (I + kG1Cols - 1) / kG1Cols, e, mt, ct)) return;
@@ -441,7 +486,8 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
 
   const int jcol = ct * kG1Cols + 32 * wave;
   const bool wave_on = jcol < I;  // I % 32 == 0
-  const int64_t grow = (int64_t)e * 2 * I + jcol + l32;
+  // (a wave past the last column streams the expert's first rows, unused)
+  const int64_t grow = (int64_t)e * 2 * I + (wave_on ? jcol : 0) + l32;
   const int64_t urow = grow + I;
   const int cpr = (FMT == MOEQ_FMT_NF4) ? H / 2 : H;  // code bytes per row
   const int spr = (FMT == MOEQ_FMT_NF4) ? H / kNf4Block : 1;
@@ -483,7 +529,7 @@ __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_
     acc0[b] = (f32x16){};
     acc1[b] = (f32x16){};
   }
-  C::run(sX, Lds<FMT>::kBuf, reinterpret_cast<const char*>(h + (int64_t)row0 * I), roff, I, q0, s0, q1, s1, on,
+  C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(h + (int64_t)row0 * I), roff, I, q0, s0, q1, s1, on,
          acc0, acc1);
   if (!on) return;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -510,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) char sX[2 * Lds<FMT>::kBuf];
+  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
   __shared__ float sw[kBM];
 
   int e, mt, ct;
@@ -522,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 
   const int ncol = ct * kG2Rows + 64 * wave;  // H % 64 == 0: a wave is all in or all out
   const bool on = ncol < H;
-  const int64_t r0 = (int64_t)e * H + ncol + l32, r1 = r0 + 32;
+  const int64_t r0 = (int64_t)e * H + (on ? ncol : 0) + l32, r1 = r0 + 32;
   const int cpr = (FMT == MOEQ_FMT_NF4) ? I / 2 : I;
   const int spr = (FMT == MOEQ_FMT_NF4) ? I / kNf4Block : 1;
 
