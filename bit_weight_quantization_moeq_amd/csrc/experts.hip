@@ -186,6 +186,35 @@ struct RowCodes {
   }
 };
 
+// Codes for a loop that never branches around its loads: the loads always
+// issue (in-range addresses) and a step outside the row or the K range is
+// zeroed through its scale alone when it is consumed.  A zero scale makes the
+// A operand exactly zero for NF4 (every table entry is a level times zero)
+// and for int8.  Masking at use keeps the load registers untouched until
+// then, so the memory counter can be waited on partially.
+template <int FMT>
+struct StreamCodes {
+  RowCodes<FMT> raw;
+  uint32_t m;
+  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K, bool ok) {
+    constexpr int half = Fmt<FMT>::kStep / 2;
+    const int kk = k0 + half * hh;
+    const bool in = ok && kk < K;
+    const int kc = in ? kk : 0;
+    const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kc / 2 : kc));
+    raw.c0 = p[0];
+    raw.c1 = p[1];
+    raw.scale = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : srow[0];
+    m = in ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));  // opaque, so the select is not folded into a branch around the loads
+  }
+  __device__ __forceinline__ RowCodes<FMT> use() const {
+    RowCodes<FMT> r = raw;
+    r.scale = __uint_as_float(__float_as_uint(raw.scale) & m);
+    return r;
+  }
+};
+
 template <int FMT>
 struct Dequant;
 
@@ -587,6 +616,218 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Decode path (few assignments, T*K <= kDecodeMax): no routing kernels and
+// no token tiles.  A workgroup owns one touched expert (its blockIdx.x-th, in
+// expert order) and one 64-row weight tile; it finds the expert and the
+// expert's assignments itself from top_k_index (ascending assignment order).
+// The 4 waves split K; each streams its share of the 64 rows' packed codes
+// straight from HBM, dequantizes them in registers into the MFMA A operand
+// and multiplies the expert's token rows (at most 32 per pass, read from L2
+// as the B operand).  The 4 partial sums meet in LDS and are added in wave
+// order, so the result does not depend on timing.  Rows of h and y are
+// indexed by assignment, so the combine needs no slot map.
+//   G1 (gate_up): tile = gate rows jcol..+32 and up rows I+jcol..+32, K = H,
+//                 B rows x[a / K]; h[a][jcol..+32] = bf16(silu(g) * u).
+//   G2 (down):    tile = down rows ncol..+64, K = I, B rows h[a];
+//                 y[a][ncol..+64] = w_a * acc.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeMax = 512;
+
+template <int FMT, bool G1>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __restrict__ act,
+                                                         const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ wts, int32_t n, int32_t Ktop,
+                                                         int32_t E, int32_t H, int32_t I,
+                                                         const uint8_t* __restrict__ wq,
+                                                         const float* __restrict__ ws,
+                                                         uint16_t* __restrict__ hout, float* __restrict__ yout) {
+  constexpr int kStep = Fmt<FMT>::kStep;
+  __shared__ uint32_t bits[MOEQ_MAX_EXPERTS / 32];
+  __shared__ int list[kDecodeMax];
+  __shared__ int s_e, s_n;
+  __shared__ float red[kWaves][2][16][64];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so the K loop is scalar
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // 1. which experts are touched
+  if (t < MOEQ_MAX_EXPERTS / 32) bits[t] = 0u;
+  __syncthreads();
+  for (int a = t; a < n; a += kThreads) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicOr(&bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  // 2. this block's expert: the blockIdx.x-th touched one; 3. its assignments
+  if (wave == 0) {
+    const int nw = (E + 31) / 32;
+    const uint32_t wbits = (lane < nw) ? bits[lane] : 0u;
+    const int c = __popc(wbits);
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    const int u = blockIdx.x;
+    const bool mine = (inc - c) <= u && u < inc;
+    const uint64_t who = __ballot(mine);
+    int e = -1;
+    if (who) {
+      const int src = __builtin_ctzll(who);
+      uint32_t wb = __shfl(wbits, src, 64);
+      int r = u - (__shfl(inc, src, 64) - __shfl(c, src, 64));
+      for (; r > 0; --r) wb &= wb - 1;  // drop the r lowest set bits
+      e = src * 32 + __builtin_ctz(wb);
+    }
+    int cnt = 0;
+    if (e >= 0) {
+      for (int base = 0; base < n; base += 64) {
+        const int a = base + lane;
+        const bool m = a < n && idx[a] == e;
+        const uint64_t mm = __ballot(m);
+        if (m) list[cnt + __popcll(mm & ((1ull << lane) - 1ull))] = a;
+        cnt += __popcll(mm);
+      }
+    }
+    if (lane == 0) {
+      s_e = e;
+      s_n = cnt;
+    }
+  }
+  __syncthreads();
+  const int e = s_e, ne = s_n;
+  if (e < 0) return;
+
+  const int K = G1 ? H : I;
+  // this block's 64 weight rows (this lane's two)
+  const int col0 = blockIdx.y * (G1 ? 32 : 64);
+  const int64_t r0 = G1 ? (int64_t)e * 2 * I + col0 + l32 : (int64_t)e * H + col0 + l32;
+  const int64_t r1 = G1 ? r0 + I : r0 + 32;
+  const int cpr = (FMT == MOEQ_FMT_NF4) ? K / 2 : K;
+  const int spr = (FMT == MOEQ_FMT_NF4) ? K / kNf4Block : 1;
+  const uint8_t* q0 = wq + r0 * cpr;
+  const uint8_t* q1 = wq + r1 * cpr;
+  const float* s0 = ws + r0 * spr;
+  const float* s1 = ws + r1 * spr;
+  // this wave's K steps
+  const int nks = (K + kStep - 1) / kStep;
+  const int ks0 = wave * nks / kWaves, ks1 = (wave + 1) * nks / kWaves;
+
+  for (int g = 0; g < ne; g += 32) {
+    const int tok = g + l32 < ne ? g + l32 : g;  // lanes past the tokens repeat one (never stored)
+    const int a = list[tok];
+    const uint16_t* brow = G1 ? act + (int64_t)(a / Ktop) * H : act + (int64_t)a * I;
+
+    f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
+    constexpr int kS = kStep / 16;
+    auto load_b = [&](bf16x8 (&xb)[kS], int ks) {
+      const int kb = ks * kStep + (kStep / 2) * hh;
+#pragma unroll
+      for (int s_ = 0; s_ < kS; ++s_) {
+        const int kk = kb + 8 * s_;
+        xb[s_] = *reinterpret_cast<const bf16x8*>(brow + (kk < K ? kk : 0));
+      }
+    };
+    // One K step: issue the next step's token fragments, multiply this
+    // step's, then refill this step's code registers two steps ahead.  Loads
+    // complete in issue order, so codes stay in flight across a step while
+    // the token fragments (L2 hits) are awaited.  Steps past the wave's range
+    // load in-range addresses and are never used.
+    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, bf16x8 (&xa)[kS], bf16x8 (&xn)[kS]) {
+      load_b(xn, ks + 1);
+      const RowCodes<FMT> c0 = sc0.use(), c1 = sc1.use();
+      Dequant<FMT> d0, d1;
+      d0.prepare(c0);
+      d1.prepare(c1);
+#pragma unroll
+      for (int s_ = 0; s_ < kS; ++s_) {
+        acc0 = mfma(d0.frag(c0, s_), xa[s_], acc0);
+        acc1 = mfma(d1.frag(c1, s_), xa[s_], acc1);
+      }
+      sc0.fetch(q0, s0, (ks + 2) * kStep, hh, K, ks + 2 < ks1);
+      sc1.fetch(q1, s1, (ks + 2) * kStep, hh, K, ks + 2 < ks1);
+    };
+    StreamCodes<FMT> ca0, ca1, cb0, cb1;
+    bf16x8 xa[kS], xb[kS];
+    ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1);
+    ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1);
+    load_b(xa, ks0);
+    cb0.fetch(q0, s0, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1);
+    cb1.fetch(q1, s1, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1);
+    // Two steps per trip with no branch between them (a branch would make the
+    // compiler copy registers that are still loading, forcing full waits): a
+    // trailing step past the range has zero codes and a zero scale, so its A
+    // operand is exactly zero and it adds nothing.
+    for (int ks = ks0; ks < ks1; ks += 2) {
+      kstep(ks, ca0, ca1, xa, xb);
+      kstep(ks + 1, cb0, cb1, xb, xa);
+    }
+    // partial sums of the 4 waves, added in wave order
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[wave][0][r][lane] = acc0[r];
+      red[wave][1][r][lane] = acc1[r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[r] = ((red[0][0][r][lane] + red[1][0][r][lane]) + red[2][0][r][lane]) + red[3][0][r][lane];
+        acc1[r] = ((red[0][1][r][lane] + red[1][1][r][lane]) + red[2][1][r][lane]) + red[3][1][r][lane];
+      }
+      if (g + l32 < ne) {
+        // lane holds, per register quad q, columns col0 + 8q + 4*hh + 0..3 of its token row
+        if (G1) {
+          uint16_t* hp = hout + (int64_t)a * I + col0 + 4 * hh;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gg = acc0[4 * q + i], uu = acc1[4 * q + i];
+              v[i] = gg * uu * __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+            }
+            *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+        } else {
+          const float wr = wts[a];
+          float* yp = yout + (int64_t)a * H + col0 + 4 * hh;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<float4*>(yp + 8 * q) =
+                make_float4(acc0[4 * q] * wr, acc0[4 * q + 1] * wr, acc0[4 * q + 2] * wr, acc0[4 * q + 3] * wr);
+            *reinterpret_cast<float4*>(yp + 32 + 8 * q) =
+                make_float4(acc1[4 * q] * wr, acc1[4 * q + 1] * wr, acc1[4 * q + 2] * wr, acc1[4 * q + 3] * wr);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Decode combine: out[t] = bf16(sum over k in order of y[t*K + k]), skipping
+// unrouted assignments.
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* __restrict__ y,
+                                                                 const int32_t* __restrict__ idx, int32_t K,
+                                                                 int32_t E, int32_t H, uint16_t* __restrict__ out) {
+  const int64_t tok = blockIdx.x;
+  for (int n4 = threadIdx.x; n4 < H / 4; n4 += kThreads) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[tok * K + k];
+      if (e < 0 || e >= E) continue;
+      const float4 v = *reinterpret_cast<const float4*>(y + (tok * K + k) * H + 4 * n4);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<uint2*>(out + tok * H + 4 * n4) =
+        make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // C1: out[t] = bf16(y[slot[t*K]] + y[slot[t*K+1]] + ... ) in k order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot,
@@ -612,9 +853,31 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 int32_t forward_tile_rows() { return kBM; }
 
+template <int FMT>
+hipError_t launch_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
+  const int32_t n = a.T * a.K;
+  const int ux = a.E < n ? a.E : n;  // at most this many experts are touched
+  const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
+  const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
+  if (ev) hipEventRecord(ev[1], s);  // no routing stage on this path
+  decode_kernel<FMT, true><<<dim3(ux, a.I / 32), kThreads, 0, s>>>(a.x, a.idx, a.wts, n, a.K, a.E, a.H, a.I, guq,
+                                                                   a.gu_s, a.h, nullptr);
+  if (ev) hipEventRecord(ev[2], s);
+  decode_kernel<FMT, false><<<dim3(ux, a.H / 64), kThreads, 0, s>>>(a.h, a.idx, a.wts, n, a.K, a.E, a.H, a.I,
+                                                                    dnq, a.dn_s, nullptr, a.y);
+  if (ev) hipEventRecord(ev[3], s);
+  decode_combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.idx, a.K, a.E, a.H, a.out);
+  if (ev) hipEventRecord(ev[4], s);
+  return hipGetLastError();
+}
+
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
   if (ev) hipEventRecord(ev[0], s);
+  if (n <= kDecodeMax) {
+    return a.format == MOEQ_FMT_NF4 ? launch_decode<MOEQ_FMT_NF4>(a, s, ev)
+                                    : launch_decode<MOEQ_FMT_INT8_ROWWISE>(a, s, ev);
+  }
   hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
   if (ev) hipEventRecord(ev[1], s);

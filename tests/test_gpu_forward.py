@@ -84,21 +84,23 @@ def test_forward_workloads_sampled(name, T, ns, nc):
     assert torch.isfinite(out.float()).all()
 
 
+# T*K = 387 takes the few-assignment path, 900 the tiled one
+@pytest.mark.parametrize("T", [129, 300])
 @pytest.mark.parametrize("fmt", ["nf4", "int8"])
-def test_forward_edge_routing(fmt):
+def test_forward_edge_routing(fmt, T):
     s = syn.SHAPES["tiny"]
-    gu, dn, x, _, _ = syn.layer_inputs(s, 129, device="cpu")
+    gu, dn, x, _, _ = syn.layer_inputs(s, T, device="cpu")
     gu, dn, x = gu.cuda(), dn.cuda(), x.cuda()
     qg, qd = _quantize(gu, fmt), _quantize(dn, fmt)
     rng = np.random.default_rng(301)
-    idx = rng.integers(-2, s.E + 2, (129, 3)).astype(np.int32)      # duplicates and unrouted
+    idx = rng.integers(-2, s.E + 2, (T, 3)).astype(np.int32)      # duplicates and unrouted
     idx[5] = [4, 4, 4]
-    wts = rng.uniform(-1, 1, (129, 3)).astype(np.float32)
+    wts = rng.uniform(-1, 1, (T, 3)).astype(np.float32)
     idx_d, wts_d = torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda()
-    say(f"forward edge routing fmt={fmt}")
+    say(f"forward edge routing fmt={fmt} T={T}")
     out = moeq.moeq_experts_forward(x, idx_d, wts_d, qg, qd)
     torch.cuda.synchronize()
-    _compare(x, idx_d, wts_d, gu, dn, fmt, out, np.arange(129), label=f"edge {fmt}")
+    _compare(x, idx_d, wts_d, gu, dn, fmt, out, np.arange(T), label=f"edge {fmt} T={T}")
     # a token with no routed assignment gets exactly zero
     idx[7] = [-1, s.E, 99]
     out2 = moeq.moeq_experts_forward(x, torch.from_numpy(idx).cuda(), wts_d, qg, qd)
@@ -126,15 +128,30 @@ def test_forward_is_bit_identical_run_to_run():
     s, fmt, gu, dn, x, idx, wts = _layer("olmoe", 4096, "cuda")
     qg, qd = _quantize(gu, fmt), _quantize(dn, fmt)
     say("forward determinism olmoe T=4096")
+
+    def fwd(lo, hi):
+        return moeq.moeq_experts_forward(x[lo:hi].contiguous(), idx[lo:hi].contiguous(),
+                                         wts[lo:hi].contiguous(), qg, qd)
     a = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
     b = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    # a token's output does not depend on the batch it is in
-    c = moeq.moeq_experts_forward(x[100:164].contiguous(), idx[100:164].contiguous(),
-                                  wts[100:164].contiguous(), qg, qd)
+    # Within each path a token's output does not depend on the batch it is in:
+    # tiled path (T*K > 512) ...
+    c = fwd(100, 400)
     torch.cuda.synchronize()
-    assert torch.equal(c, a[100:164])
+    assert torch.equal(c[:64], a[100:164])
+    # ... and the few-assignment path (T*K <= 512), run to run as well
+    d1, d2, d3 = fwd(100, 164), fwd(100, 164), fwd(100, 132)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2)
+    assert torch.equal(d3, d1[:32])
+    # The two paths add the K products in different orders; they agree to
+    # well within the forward tolerance.
+    err = rel_frobenius(bf16_to_f32(host_bits(d1)).astype(np.float64),
+                        bf16_to_f32(host_bits(a[100:164])).astype(np.float64))
+    print(f"few-assignment vs tiled path: rel Frobenius {err:.3e}")
+    assert err <= TOL / 4
 
 
 def test_forward_rejects_mixed_formats():
