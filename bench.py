@@ -8,12 +8,15 @@ top-8 uniform routing straight from that packed storage (routing buckets,
 gate_up grouped GEMM + SwiGLU, down grouped GEMM, k-ordered combine).
 
 Printed (one JSON line): ``value`` = experts-forward tokens/s (HIP events
-around the forward of every timed step), ``quantize_GBps`` = quantize
-algorithmic bytes / quantize time (events), ``ms_per_step`` = wall time per
-whole step; ``roofline`` for the dominant kernel of the step, from its own
-events; ``decode`` = forward-only figures at T = 1 and 32; ``cpu_baseline`` =
-the CPU oracle on a bounded sample of the same workload.  Inputs are seeded
-synthetic tensors resident in HBM before the timed region.
+around the forward of the timed steps that record no stage events),
+``quantize_GBps`` = quantize algorithmic bytes / quantize time (events),
+``ms_per_step`` = wall time per whole step; ``roofline`` for the dominant
+kernel of the step, from the stage events recorded on every other timed step;
+``device_copy_GBps`` = a plain 1 GiB device copy, the measured HBM ceiling;
+``decode`` = forward-only figures at T = 1 and 32, streaming the weights from
+HBM; ``codec`` = row-wise int8 quantize and the two dequantizes;
+``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
+Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
 
 import argparse
@@ -42,6 +45,7 @@ def parse():
     ap.add_argument("--T", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-codec", action="store_true")
     return ap.parse_args()
 
 
@@ -101,6 +105,110 @@ def cpu_baseline(s, gu, dn, x, idx, wts, T):
     }
 
 
+def device_copy_GBps(torch, dev, nbytes=1 << 30, reps=10):
+    """Measured HBM bandwidth of a plain device copy (read + write bytes / time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, calls=48):
+    """Forward-only figures at T = 1 and 32.  The calls rotate over `layers`
+    copies of the quantized layer (together larger than the last-level cache),
+    so every call streams its experts' codes from HBM as in a many-layer model;
+    `calls` back-to-back calls sit between one pair of events.  A second pass
+    with stage events gives the per-kernel split."""
+    stack = [(qg, qd)]
+    for _ in range(layers - 1):
+        c = lambda q: moeq.QWeight(q.format, q.num_experts, q.rows, q.cols, q.qdata.clone(), q.scales.clone())
+        stack.append((c(qg), c(qd)))
+    dec = {}
+    for Td in (1, 32):
+        xd = syn.hidden_states(Td, s.H, device=dev, layer=1)
+        idd, wd = syn.routing(Td, s.K, s.E, kind=s.routing, device=dev, layer=1)
+        od = torch.empty((Td, s.H), dtype=torch.bfloat16, device=dev)
+        wsd = torch.empty(moeq.moeq_experts_forward_workspace_bytes(Td, s.K, qg, qd), dtype=torch.uint8, device=dev)
+        for r in range(2 * layers):
+            g, d = stack[r % layers]
+            moeq.moeq_experts_forward(xd, idd, wd, g, d, out=od, workspace=wsd)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(calls):
+            g, d = stack[r % layers]
+            moeq.moeq_experts_forward(xd, idd, wd, g, d, out=od, workspace=wsd)
+        b.record()
+        torch.cuda.synchronize()
+        tms = a.elapsed_time(b) / calls
+        reps = 4 * layers
+        evd = [new_events(torch, 5) for _ in range(reps)]
+        for r in range(reps):
+            g, d = stack[r % layers]
+            moeq.moeq_experts_forward(xd, idd, wd, g, d, out=od, workspace=wsd,
+                                      stage_events=[h.cuda_event for h in evd[r]])
+        torch.cuda.synchronize()
+        kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evd[layers:]]))
+               for j, n in enumerate(["route", "g1_gate_up_swiglu", "g2_down", "combine"])}
+        nb, fl, Ud = forward_bytes_flops(s, idd.cpu().numpy(), Td)
+        dec[f"T{Td}"] = {"tokens_per_s": Td / (tms * 1e-3), "forward_ms": tms,
+                         "packed_GBps": nb / (tms * 1e-3) / 1e9,
+                         "hbm_frac": nb / (tms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "copy_frac": nb / (tms * 1e-3) / 1e9 / copy_GBps,
+                         "touched_experts": Ud, "stage_ms_with_events": kms,
+                         "timing": f"{calls} back-to-back calls over {layers} layer copies"}
+    return dec
+
+
+def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
+    """Row-wise int8 quantize on the gpt-oss-shaped experts and dequantize of
+    both formats: algorithmic bytes / event time."""
+    out = {}
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    g = syn.SHAPES["gptoss"]
+    wg = syn.expert_weights(g.gate_up_shape, tensor=syn.GATE_UP, device=dev)
+    wd = syn.expert_weights(g.down_shape, tensor=syn.DOWN, device=dev)
+    q8g = moeq.QWeight.empty(moeq.FMT_INT8_ROWWISE, *g.gate_up_shape, device=dev)
+    q8d = moeq.QWeight.empty(moeq.FMT_INT8_ROWWISE, *g.down_shape, device=dev)
+    ms = timed(lambda: (moeq.moeq_quantize_int8_rowwise(wg, out=q8g), moeq.moeq_quantize_int8_rowwise(wd, out=q8d)))
+    nel = wg.numel() + wd.numel()
+    nrow = g.E * (g.gate_up_shape[1] + g.down_shape[1])
+    b = 3.0 * nel + 4.0 * nrow
+    out["int8_quantize"] = {"workload": f"gpt-oss-shaped gate_up {list(g.gate_up_shape)} + down {list(g.down_shape)}",
+                            "ms": ms, "GBps": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                            "copy_frac": b / (ms * 1e-3) / 1e9 / copy_GBps}
+    dq = torch.empty(g.gate_up_shape, dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: moeq.moeq_dequantize(q8g, out=dq))
+    b = 3.0 * wg.numel() + 4.0 * g.E * g.gate_up_shape[1]
+    out["int8_dequantize"] = {"workload": f"gpt-oss-shaped gate_up {list(g.gate_up_shape)}", "ms": ms,
+                              "GBps": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    q4 = moeq.moeq_quantize_nf4(wg)
+    ms = timed(lambda: moeq.moeq_dequantize(q4, out=dq))
+    b = wg.numel() * NF4_BYTES_PER_ELEM
+    out["nf4_dequantize"] = {"workload": f"gpt-oss-shaped gate_up {list(g.gate_up_shape)}", "ms": ms,
+                             "GBps": b / (ms * 1e-3) / 1e9, "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del wg, wd, q8g, q8d, dq, q4
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -129,41 +237,56 @@ def main():
     qd = moeq.QWeight.empty(moeq.FMT_NF4, *s.down_shape, device=dev)
     out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+    copy_GBps = device_copy_GBps(torch, dev)
+
     nsteps = args.warmup + args.steps
     ev = [new_events(torch, 8) for _ in range(nsteps)]
 
-    def step(e):
-        # every library call runs on torch's current stream, where these events are recorded
+    def step(i):
+        # Every library call runs on torch's current stream, where these events
+        # are recorded.  Even steps also record the forward's stage boundaries
+        # (per-kernel durations); odd steps record only its start and end, so
+        # the forward time carries no event gaps between its kernels.
+        e = ev[i]
         e[0].record()
         moeq.moeq_quantize_nf4(gu, out=qg)
         e[1].record()
         moeq.moeq_quantize_nf4(dn, out=qd)
         e[2].record()
-        moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=out, workspace=ws,
-                                  stage_events=[h.cuda_event for h in e[3:8]])
+        if i % 2 == 0:
+            moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=out, workspace=ws,
+                                      stage_events=[h.cuda_event for h in e[3:8]])
+        else:
+            e[3].record()
+            moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=out, workspace=ws)
+            e[7].record()
 
     for i in range(args.warmup):
-        step(ev[i])
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, nsteps):
-        step(ev[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
     names = ["quantize_gate_up", "quantize_down", None, "route", "g1_gate_up_swiglu", "g2_down", "combine"]
     stage = {n: [] for n in names if n}
-    fwd_ms, q_ms = [], []
+    fwd_plain, fwd_staged, q_ms = [], [], []
     for i in range(args.warmup, nsteps):
         e = ev[i]
-        for j, n in enumerate(names):
-            if n:
-                stage[n].append(e[j].elapsed_time(e[j + 1]))
         q_ms.append(e[0].elapsed_time(e[2]))
-        fwd_ms.append(e[3].elapsed_time(e[7]))
-    avg = {n: float(np.mean(v)) for n, v in stage.items()}
-    fwd = float(np.mean(fwd_ms))
+        stage["quantize_gate_up"].append(e[0].elapsed_time(e[1]))
+        stage["quantize_down"].append(e[1].elapsed_time(e[2]))
+        if i % 2 == 0:
+            for j in range(3, 7):
+                stage[names[j]].append(e[j].elapsed_time(e[j + 1]))
+            fwd_staged.append(e[3].elapsed_time(e[7]))
+        else:
+            fwd_plain.append(e[3].elapsed_time(e[7]))
+    avg = {n: float(np.mean(v)) for n, v in stage.items() if v}
+    fwd = float(np.mean(fwd_plain or fwd_staged))
     qt = float(np.mean(q_ms))
 
     n_gu, n_dn = int(np.prod(s.gate_up_shape)), int(np.prod(s.down_shape))
@@ -207,39 +330,23 @@ def main():
                                 f"then the experts forward from packed storage"),
                    "E": s.E, "H": s.H, "I": s.I, "K": s.K, "T": T, "format": "nf4", "blocksize": 64},
         "forward_ms": fwd,
+        "forward_ms_with_stage_events": float(np.mean(fwd_staged)) if fwd_staged else None,
         "forward_TFLOPs": f_flops / (fwd * 1e-3) / 1e12,
         "forward_mfma_frac": f_flops / (fwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "quantize_ms": qt,
         "quantize_GBps": q_bytes / (qt * 1e-3) / 1e9,
         "quantize_hbm_frac": q_bytes / (qt * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "quantize_copy_frac": q_bytes / (qt * 1e-3) / 1e9 / copy_GBps,
+        "device_copy_GBps": copy_GBps,
         "stage_ms": avg,
         "touched_experts": U,
         "roofline": roof,
     }
 
     if not args.no_decode:
-        dec = {}
-        for Td in (1, 32):
-            xd = syn.hidden_states(Td, s.H, device=dev, layer=1)
-            idd, wd = syn.routing(Td, s.K, s.E, kind=s.routing, device=dev, layer=1)
-            od = torch.empty((Td, s.H), dtype=torch.bfloat16, device=dev)
-            wsd = torch.empty(moeq.moeq_experts_forward_workspace_bytes(Td, s.K, qg, qd),
-                              dtype=torch.uint8, device=dev)
-            reps = 50
-            evd = [new_events(torch, 5) for _ in range(reps + 5)]
-            for r in range(reps + 5):
-                moeq.moeq_experts_forward(xd, idd, wd, qg, qd, out=od, workspace=wsd,
-                                          stage_events=[h.cuda_event for h in evd[r]])
-            torch.cuda.synchronize()
-            tms = float(np.mean([e[0].elapsed_time(e[4]) for e in evd[5:]]))
-            kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evd[5:]]))
-                   for j, n in enumerate(["route", "g1_gate_up_swiglu", "g2_down", "combine"])}
-            b, fl, Ud = forward_bytes_flops(s, idd.cpu().numpy(), Td)
-            dec[f"T{Td}"] = {"tokens_per_s": Td / (tms * 1e-3), "forward_ms": tms,
-                             "packed_GBps": b / (tms * 1e-3) / 1e9,
-                             "hbm_frac": b / (tms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                             "touched_experts": Ud, "stage_ms": kms}
-        result["decode"] = dec
+        result["decode"] = decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps)
+    if not args.no_codec:
+        result["codec"] = codec_figures(torch, np, moeq, syn, dev, copy_GBps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, gu, dn, x, idx, wts, T)

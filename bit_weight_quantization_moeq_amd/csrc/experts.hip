@@ -196,7 +196,11 @@ template <int FMT>
 struct StreamCodes {
   RowCodes<FMT> raw;
   uint32_t m;
-  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K, bool ok) {
+  // row_scale: the int8 row scale, loaded once by the caller (a per-step
+  // load of a loop-invariant value would be hoisted to just before the loop
+  // and make every step wait for it); unused for NF4.
+  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K, bool ok,
+                                        float row_scale) {
     constexpr int half = Fmt<FMT>::kStep / 2;
     const int kk = k0 + half * hh;
     const bool in = ok && kk < K;
@@ -204,7 +208,7 @@ struct StreamCodes {
     const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kc / 2 : kc));
     raw.c0 = p[0];
     raw.c1 = p[1];
-    raw.scale = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : srow[0];
+    raw.scale = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : row_scale;
     m = in ? 0xffffffffu : 0u;
     asm volatile("" : "+v"(m));  // opaque, so the select is not folded into a branch around the loads
   }
@@ -618,49 +622,68 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // Decode path (few assignments, T*K <= kDecodeMax): no routing kernels and
 // no token tiles.  A workgroup owns one touched expert (its blockIdx.x-th, in
-// expert order) and one 64-row weight tile; it finds the expert and the
-// expert's assignments itself from top_k_index (ascending assignment order).
-// The 4 waves split K; each streams its share of the 64 rows' packed codes
-// straight from HBM, dequantizes them in registers into the MFMA A operand
-// and multiplies the expert's token rows (at most 32 per pass, read from L2
-// as the B operand).  The 4 partial sums meet in LDS and are added in wave
-// order, so the result does not depend on timing.  Rows of h and y are
-// indexed by assignment, so the combine needs no slot map.
-//   G1 (gate_up): tile = gate rows jcol..+32 and up rows I+jcol..+32, K = H,
-//                 B rows x[a / K]; h[a][jcol..+32] = bf16(silu(g) * u).
-//   G2 (down):    tile = down rows ncol..+64, K = I, B rows h[a];
+// expert order) and RB row blocks of 64 weight rows; it finds the expert and
+// the expert's assignments itself from top_k_index (ascending assignment
+// order).  Its NW waves are RB row blocks x P parts of K (NW = RB * P, P
+// chosen on the host so that few touched experts still fill the chip).  Each
+// wave streams its part of its 64 rows' packed codes straight from HBM,
+// dequantizes them in registers into the MFMA A operand and multiplies the
+// expert's token rows (at most 32 per pass, read from L2 as the B operand).
+// The P partial sums of a row block meet in LDS and are added in part order,
+// so the result does not depend on timing.  Rows of h and y are indexed by
+// assignment, so the combine needs no slot map.
+//   G1 (gate_up): row block = gate rows jcol..+32 and up rows I+jcol..+32,
+//                 K = H, B rows x[a / K]; h[a][jcol..+32] = bf16(silu(g) * u).
+//   G2 (down):    row block = down rows ncol..+64, K = I, B rows h[a];
 //                 y[a][ncol..+64] = w_a * acc.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeMax = 512;
 
-template <int FMT, bool G1>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __restrict__ act,
-                                                         const int32_t* __restrict__ idx,
-                                                         const float* __restrict__ wts, int32_t n, int32_t Ktop,
-                                                         int32_t E, int32_t H, int32_t I,
-                                                         const uint8_t* __restrict__ wq,
-                                                         const float* __restrict__ ws,
-                                                         uint16_t* __restrict__ hout, float* __restrict__ yout) {
+// LDS-only barrier: waits for this wave's LDS traffic, not for its global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int FMT, bool G1, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restrict__ act,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ wts, int32_t n, int32_t Ktop,
+                                                        int32_t E, int32_t H, int32_t I, int32_t P,
+                                                        const uint8_t* __restrict__ wq,
+                                                        const float* __restrict__ ws,
+                                                        uint16_t* __restrict__ hout, float* __restrict__ yout) {
+  constexpr int kT = NW * 64;
+  constexpr int kJ = kDecodeMax / kT;  // assignments per thread
   constexpr int kStep = Fmt<FMT>::kStep;
+  constexpr int kS = kStep / 16;
   __shared__ uint32_t bits[MOEQ_MAX_EXPERTS / 32];
   __shared__ int list[kDecodeMax];
-  __shared__ int s_e, s_n;
-  __shared__ float red[kWaves][2][16][64];
+  __shared__ int cnt[kDecodeMax / 64];
+  __shared__ float red[NW][2][16][64];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, so the K loop is scalar
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // 1. which experts are touched
-  if (t < MOEQ_MAX_EXPERTS / 32) bits[t] = 0u;
-  __syncthreads();
-  for (int a = t; a < n; a += kThreads) {
-    const int e = idx[a];
-    if (e >= 0 && e < E) atomicOr(&bits[e >> 5], 1u << (e & 31));
+  // 1. this thread's assignments (a = t + j*kT) and the set of touched experts
+  int my[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int a = t + j * kT;
+    my[j] = a < n ? idx[a] : -1;
   }
-  __syncthreads();
-  // 2. this block's expert: the blockIdx.x-th touched one; 3. its assignments
-  if (wave == 0) {
+  if (t < MOEQ_MAX_EXPERTS / 32) bits[t] = 0u;
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)
+    if (my[j] >= 0 && my[j] < E) atomicOr(&bits[my[j] >> 5], 1u << (my[j] & 31));
+  lds_barrier();
+
+  // 2. this block's expert: the blockIdx.x-th touched one (every wave finds it)
+  int e = -1;
+  {
     const int nw = (E + 31) / 32;
     const uint32_t wbits = (lane < nw) ? bits[lane] : 0u;
     const int c = __popc(wbits);
@@ -671,38 +694,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __rest
       if (lane >= o) inc += v;
     }
     const int u = blockIdx.x;
-    const bool mine = (inc - c) <= u && u < inc;
-    const uint64_t who = __ballot(mine);
-    int e = -1;
+    const uint64_t who = __ballot((inc - c) <= u && u < inc);
     if (who) {
       const int src = __builtin_ctzll(who);
       uint32_t wb = __shfl(wbits, src, 64);
-      int r = u - (__shfl(inc, src, 64) - __shfl(c, src, 64));
-      for (; r > 0; --r) wb &= wb - 1;  // drop the r lowest set bits
+      for (int r = u - (__shfl(inc, src, 64) - __shfl(c, src, 64)); r > 0; --r) wb &= wb - 1;
       e = src * 32 + __builtin_ctz(wb);
     }
-    int cnt = 0;
-    if (e >= 0) {
-      for (int base = 0; base < n; base += 64) {
-        const int a = base + lane;
-        const bool m = a < n && idx[a] == e;
-        const uint64_t mm = __ballot(m);
-        if (m) list[cnt + __popcll(mm & ((1ull << lane) - 1ull))] = a;
-        cnt += __popcll(mm);
-      }
-    }
-    if (lane == 0) {
-      s_e = e;
-      s_n = cnt;
-    }
+    e = __builtin_amdgcn_readfirstlane(e);
   }
-  __syncthreads();
-  const int e = s_e, ne = s_n;
-  if (e < 0) return;
+  if (e < 0) return;  // the whole block: the bitmap is shared
 
+  // 3. this wave's row block and part of K; start its first codes now
   const int K = G1 ? H : I;
-  // this block's 64 weight rows (this lane's two)
-  const int col0 = blockIdx.y * (G1 ? 32 : 64);
+  const int nrb = G1 ? I / 32 : H / 64;  // row blocks of the expert
+  const int RB = NW / P;
+  const int rbi = blockIdx.y * RB + wave / P, part = wave % P;
+  const bool on = rbi < nrb;  // a wave past the last row block streams block 0 and stores nothing
+  const int col0 = (on ? rbi : 0) * (G1 ? 32 : 64);
   const int64_t r0 = G1 ? (int64_t)e * 2 * I + col0 + l32 : (int64_t)e * H + col0 + l32;
   const int64_t r1 = G1 ? r0 + I : r0 + 32;
   const int cpr = (FMT == MOEQ_FMT_NF4) ? K / 2 : K;
@@ -711,17 +720,45 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __rest
   const uint8_t* q1 = wq + r1 * cpr;
   const float* s0 = ws + r0 * spr;
   const float* s1 = ws + r1 * spr;
-  // this wave's K steps
-  const int nks = (K + kStep - 1) / kStep;
-  const int ks0 = wave * nks / kWaves, ks1 = (wave + 1) * nks / kWaves;
+  const int nks = (K + kStep - 1) / kStep, nkp = (nks + 1) / 2;  // steps, pairs of steps
+  const int ks0 = 2 * (part * nkp / P), ks1 = min(2 * ((part + 1) * nkp / P), nks);
+  // int8: the row scales, first of this wave's loads
+  const float rs0 = (FMT == MOEQ_FMT_NF4) ? 0.0f : s0[0];
+  const float rs1 = (FMT == MOEQ_FMT_NF4) ? 0.0f : s1[0];
+  StreamCodes<FMT> ca0, ca1, cb0, cb1;
+  ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1, rs0);
+  ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1, rs1);
+
+  // 4. the expert's assignments in ascending order: chunk c = a / 64 is
+  //    wave c % NW's j = c / NW values
+  uint64_t bal[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    bal[j] = __ballot(my[j] == e);
+    if (lane == 0) cnt[wave + j * NW] = __popcll(bal[j]);
+  }
+  lds_barrier();
+  int ne = 0;
+#pragma unroll
+  for (int c = 0; c < kDecodeMax / 64; ++c) ne += cnt[c];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    int base = 0;
+    for (int c = 0; c < wave + j * NW; ++c) base += cnt[c];
+    if (my[j] == e) list[base + __popcll(bal[j] & ((1ull << lane) - 1ull))] = t + j * kT;
+  }
+  lds_barrier();
 
   for (int g = 0; g < ne; g += 32) {
     const int tok = g + l32 < ne ? g + l32 : g;  // lanes past the tokens repeat one (never stored)
     const int a = list[tok];
     const uint16_t* brow = G1 ? act + (int64_t)(a / Ktop) * H : act + (int64_t)a * I;
+    if (g > 0) {
+      ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1, rs0);
+      ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1, rs1);
+    }
 
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
-    constexpr int kS = kStep / 16;
     auto load_b = [&](bf16x8 (&xb)[kS], int ks) {
       const int kb = ks * kStep + (kStep / 2) * hh;
 #pragma unroll
@@ -734,8 +771,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __rest
     // step's, then refill this step's code registers two steps ahead.  Loads
     // complete in issue order, so codes stay in flight across a step while
     // the token fragments (L2 hits) are awaited.  Steps past the wave's range
-    // load in-range addresses and are never used.
+    // load in-range addresses and are zeroed through their scale.
     auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, bf16x8 (&xa)[kS], bf16x8 (&xn)[kS]) {
+      // keep each step's arithmetic after the previous step's (hoisting it
+      // would wait for codes that are still loading)
+      __builtin_amdgcn_sched_barrier(0);
       load_b(xn, ks + 1);
       const RowCodes<FMT> c0 = sc0.use(), c1 = sc1.use();
       Dequant<FMT> d0, d1;
@@ -746,81 +786,109 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint16_t* __rest
         acc0 = mfma(d0.frag(c0, s_), xa[s_], acc0);
         acc1 = mfma(d1.frag(c1, s_), xa[s_], acc1);
       }
-      sc0.fetch(q0, s0, (ks + 2) * kStep, hh, K, ks + 2 < ks1);
-      sc1.fetch(q1, s1, (ks + 2) * kStep, hh, K, ks + 2 < ks1);
+      sc0.fetch(q0, s0, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs0);
+      sc1.fetch(q1, s1, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs1);
     };
-    StreamCodes<FMT> ca0, ca1, cb0, cb1;
     bf16x8 xa[kS], xb[kS];
-    ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1);
-    ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1);
     load_b(xa, ks0);
-    cb0.fetch(q0, s0, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1);
-    cb1.fetch(q1, s1, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1);
-    // Two steps per trip with no branch between them (a branch would make the
-    // compiler copy registers that are still loading, forcing full waits): a
-    // trailing step past the range has zero codes and a zero scale, so its A
-    // operand is exactly zero and it adds nothing.
+    cb0.fetch(q0, s0, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs0);
+    cb1.fetch(q1, s1, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs1);
+    // Two steps per trip, register sets alternating, with no branch between
+    // them (a branch there would make the compiler copy or re-load register
+    // sets that are still loading, forcing full waits).  Parts are whole
+    // pairs of steps, so only the last part of an odd step count runs a
+    // trailing step past the range: its scale is zero, its A operand exactly
+    // zero, and it adds nothing.
     for (int ks = ks0; ks < ks1; ks += 2) {
       kstep(ks, ca0, ca1, xa, xb);
       kstep(ks + 1, cb0, cb1, xb, xa);
     }
-    // partial sums of the 4 waves, added in wave order
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      red[wave][0][r][lane] = acc0[r];
-      red[wave][1][r][lane] = acc1[r];
-    }
-    __syncthreads();
-    if (wave == 0) {
+
+    // the P partial sums of each row block, added in part order
+    bool owner = true;
+    if (P > 1) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        acc0[r] = ((red[0][0][r][lane] + red[1][0][r][lane]) + red[2][0][r][lane]) + red[3][0][r][lane];
-        acc1[r] = ((red[0][1][r][lane] + red[1][1][r][lane]) + red[2][1][r][lane]) + red[3][1][r][lane];
+        red[wave][0][r][lane] = acc0[r];
+        red[wave][1][r][lane] = acc1[r];
       }
-      if (g + l32 < ne) {
-        // lane holds, per register quad q, columns col0 + 8q + 4*hh + 0..3 of its token row
-        if (G1) {
-          uint16_t* hp = hout + (int64_t)a * I + col0 + 4 * hh;
+      lds_barrier();
+      owner = part == 0;
+      if (owner) {
+        // unrolled over the largest P so that the LDS reads are all in flight
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[4];
+        for (int p = 1; p < NW; ++p) {
+          if (p < P) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float gg = acc0[4 * q + i], uu = acc1[4 * q + i];
-              v[i] = gg * uu * __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+            for (int r = 0; r < 16; ++r) {
+              acc0[r] += red[wave + p][0][r][lane];
+              acc1[r] += red[wave + p][1][r][lane];
             }
-            *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          }
-        } else {
-          const float wr = wts[a];
-          float* yp = yout + (int64_t)a * H + col0 + 4 * hh;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<float4*>(yp + 8 * q) =
-                make_float4(acc0[4 * q] * wr, acc0[4 * q + 1] * wr, acc0[4 * q + 2] * wr, acc0[4 * q + 3] * wr);
-            *reinterpret_cast<float4*>(yp + 32 + 8 * q) =
-                make_float4(acc1[4 * q] * wr, acc1[4 * q + 1] * wr, acc1[4 * q + 2] * wr, acc1[4 * q + 3] * wr);
           }
         }
       }
     }
-    __syncthreads();
+    if (owner && on && g + l32 < ne) {
+      // lane holds, per register quad q, rows col0 + 8q + 4*hh + 0..3 of its token
+      if (G1) {
+        uint16_t* hp = hout + (int64_t)a * I + col0 + 4 * hh;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gg = acc0[4 * q + i], uu = acc1[4 * q + i];
+            v[i] = gg * uu * __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+          }
+          *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      } else {
+        const float wr = wts[a];
+        float* yp = yout + (int64_t)a * H + col0 + 4 * hh;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<float4*>(yp + 8 * q) =
+              make_float4(acc0[4 * q] * wr, acc0[4 * q + 1] * wr, acc0[4 * q + 2] * wr, acc0[4 * q + 3] * wr);
+          *reinterpret_cast<float4*>(yp + 32 + 8 * q) =
+              make_float4(acc1[4 * q] * wr, acc1[4 * q + 1] * wr, acc1[4 * q + 2] * wr, acc1[4 * q + 3] * wr);
+        }
+      }
+    }
+    if (P > 1) lds_barrier();  // red is reused by the next token group
   }
 }
 
 // Decode combine: out[t] = bf16(sum over k in order of y[t*K + k]), skipping
-// unrouted assignments.
+// unrouted assignments.  One workgroup per token: the routing entries are
+// read once into LDS, then each thread keeps the y loads of up to 8
+// assignments in flight at once.
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* __restrict__ y,
                                                                  const int32_t* __restrict__ idx, int32_t K,
                                                                  int32_t E, int32_t H, uint16_t* __restrict__ out) {
+  __shared__ uint8_t routed[kDecodeMax];
   const int64_t tok = blockIdx.x;
+  for (int k = threadIdx.x; k < K; k += kThreads) {
+    const int e = idx[tok * K + k];
+    routed[k] = e >= 0 && e < E;
+  }
+  __syncthreads();
   for (int n4 = threadIdx.x; n4 < H / 4; n4 += kThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[tok * K + k];
-      if (e < 0 || e >= E) continue;
-      const float4 v = *reinterpret_cast<const float4*>(y + (tok * K + k) * H + 4 * n4);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      bool use[8];
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        use[j] = k0 + j < K && routed[k0 + j];
+        v[j] = use[j] ? *reinterpret_cast<const float4*>(y + (tok * K + k0 + j) * H + 4 * n4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (use[j]) {
+          acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
+        }
+      }
     }
     *reinterpret_cast<uint2*>(out + tok * H + 4 * n4) =
         make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
@@ -853,18 +921,36 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 int32_t forward_tile_rows() { return kBM; }
 
+// Decode launch shape: 4 waves per workgroup split as RB row blocks x P
+// parts of K.  P grows until the touched experts' row blocks give enough
+// waves to fill the chip (~6 per CU).
+struct DecodeShape {
+  int p, rb, gy;
+};
+DecodeShape decode_shape(int ux, int nrb) {
+  const long w1 = (long)ux * nrb;  // waves at P = 1
+  const int p = w1 >= 1536 ? 1 : (2 * w1 >= 1536 ? 2 : 4);
+  const int rb = kWaves / p;
+  return {p, rb, (nrb + rb - 1) / rb};
+}
+
+template <int FMT, bool G1>
+void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const uint8_t* q, const float* sc,
+                        hipStream_t s) {
+  const int32_t n = a.T * a.K;
+  const DecodeShape d = decode_shape(ux, G1 ? a.I / 32 : a.H / 64);
+  decode_kernel<FMT, G1, kWaves><<<dim3(ux, d.gy), kThreads, 0, s>>>(act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p,
+                                                                     q, sc, a.h, a.y);
+}
+
 template <int FMT>
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
   const int ux = a.E < n ? a.E : n;  // at most this many experts are touched
-  const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
-  const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   if (ev) hipEventRecord(ev[1], s);  // no routing stage on this path
-  decode_kernel<FMT, true><<<dim3(ux, a.I / 32), kThreads, 0, s>>>(a.x, a.idx, a.wts, n, a.K, a.E, a.H, a.I, guq,
-                                                                   a.gu_s, a.h, nullptr);
+  launch_decode_gemm<FMT, true>(a, ux, a.x, static_cast<const uint8_t*>(a.gu_q), a.gu_s, s);
   if (ev) hipEventRecord(ev[2], s);
-  decode_kernel<FMT, false><<<dim3(ux, a.H / 64), kThreads, 0, s>>>(a.h, a.idx, a.wts, n, a.K, a.E, a.H, a.I,
-                                                                    dnq, a.dn_s, nullptr, a.y);
+  launch_decode_gemm<FMT, false>(a, ux, a.h, static_cast<const uint8_t*>(a.dn_q), a.dn_s, s);
   if (ev) hipEventRecord(ev[3], s);
   decode_combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.idx, a.K, a.E, a.H, a.out);
   if (ev) hipEventRecord(ev[4], s);

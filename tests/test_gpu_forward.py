@@ -113,6 +113,24 @@ def test_forward_edge_routing(fmt, T):
     _compare(x[:1], idx_d[:1, :1], wts_d[:1, :1], gu, dn, fmt, out1, [0], label=f"T=1 K=1 {fmt}")
 
 
+# K larger than a wave: T*K = 280 takes the few-assignment path, 560 the tiled one
+@pytest.mark.parametrize("T", [4, 8])
+def test_forward_large_top_k(T):
+    s = syn.SHAPES["tiny"]
+    gu, dn, x, _, _ = syn.layer_inputs(s, T, device="cpu")
+    gu, dn, x = gu.cuda(), dn.cuda(), x.cuda()
+    qg, qd = moeq.moeq_quantize_nf4(gu), moeq.moeq_quantize_nf4(dn)
+    rng = np.random.default_rng(17)
+    K = 70
+    idx = rng.integers(-1, s.E + 1, (T, K)).astype(np.int32)
+    wts = rng.uniform(-0.2, 0.2, (T, K)).astype(np.float32)
+    idx_d, wts_d = torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda()
+    say(f"forward large top-k T={T} K={K}")
+    out = moeq.moeq_experts_forward(x, idx_d, wts_d, qg, qd)
+    torch.cuda.synchronize()
+    _compare(x, idx_d, wts_d, gu, dn, "nf4", out, np.arange(T), label=f"K={K} T={T}")
+
+
 def test_forward_empty_batch():
     s = syn.SHAPES["tiny"]
     gu, dn = syn.expert_weights(s.gate_up_shape, device="cuda"), syn.expert_weights(s.down_shape, device="cuda")
