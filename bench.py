@@ -59,6 +59,30 @@ def forward_bytes_flops(s, idx_np, T):
     return wbytes + abytes, flops, U
 
 
+PROFILE_KERNEL = {"g1_gate_up_swiglu": "g1_kernel<1>", "g2_down": "g2_kernel<1>",
+                  "quantize_gate_up": "nf4_quantize_kernel", "quantize_down": "nf4_quantize_kernel",
+                  "combine": "combine_kernel"}
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the stage's kernel from the committed
+    FETCH_SIZE/WRITE_SIZE summaries under profiles/, or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    import glob
+    import re
+
+    from bit_weight_quantization_moeq_amd.profsum import source_hash
+    want = PROFILE_KERNEL.get(stage)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+        if not m:
+            continue
+        block = json.loads(m.group(1))
+        if block.get("kernel") == want and block.get("source_sha256") == source_hash():
+            return float(block["traffic_bytes"])
+    return None
+
+
 def new_events(torch, n):
     """n timing events on torch's current stream, created now (one record each)
     so their raw hipEvent_t handles can be handed to the library."""
@@ -314,6 +338,7 @@ def main():
         achieved = amount / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["ms_per_launch"] = avg[dom]
 

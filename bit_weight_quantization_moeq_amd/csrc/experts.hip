@@ -5,21 +5,36 @@
 // down_proj [E, H, I], act_fn between them; unsloth-zoo issue #850,
 // Suggested fix: the (hidden_states, top_k_index, top_k_weights) interface).
 //
-// After the routing stage has sorted the assignments by expert:
-//   G1  grouped GEMM over tiles (expert, 128 sorted assignments, 128 columns of
-//       h): gathered bf16 rows of x times the gate and up weight rows, with
-//       fp32 accumulation on v_mfma_f32_32x32x16_bf16; the epilogue pairs gate
-//       column j with up column j and writes h = bf16(silu(g) * u).
-//   G2  the same machinery over (expert, 128 sorted rows, 256 output columns):
-//       h times the down rows, scaled by the routing weight in fp32 -> y.
-//   C1  out[t] = bf16(sum over k = 0..K-1, in that order, of y[slot[t*K+k]]).
-// No float atomics anywhere: every output element has one writer, so the
-// forward is bit-identical run to run and independent of the batch.
+// Two paths, chosen by the number of assignments n = T*K:
 //
-// Data flow inside a GEMM workgroup (4 waves):
+// Tiled path (n > 512), after the routing stage has sorted the assignments
+// by expert:
+//   G1  grouped GEMM over tiles (expert, up to 256 sorted assignments, 128
+//       columns of h): gathered bf16 rows of x times the gate and up weight
+//       rows, fp32 accumulation on v_mfma_f32_32x32x16_bf16; the epilogue
+//       pairs gate column j with up column j and writes h = bf16(silu(g) * u).
+//   G2  the same machinery over (expert, up to 256 sorted rows, 256 output
+//       columns): h times the down rows, scaled by the routing weight in fp32
+//       -> y.
+//   C1  out[t] = bf16(sum over k = 0..K-1, in that order, of y[slot[t*K+k]]).
+//
+// Few-assignment path (n <= 512, decode): no routing kernels and no token
+// tiles; each workgroup finds its expert and that expert's assignments from
+// top_k_index itself, streams weight codes straight from HBM into registers
+// and splits K across its waves when few experts are touched (see
+// decode_kernel).  h and y rows are indexed by assignment.
+//
+// No float atomics anywhere: every output element has one writer and every
+// sum has a fixed order, so the forward is bit-identical run to run, and a
+// token's output does not depend on the other tokens of the batch within a
+// path.  The two paths add the K products in different orders.
+//
+// Data flow inside a tiled-GEMM workgroup (4 waves):
 //   * The token rows of the tile (x rows gathered through perm, or h rows)
-//     stream through a double-buffered LDS tile, one K step ahead, shared by
-//     the 4 waves: they are the MFMA B operand.
+//     stream through 2 or 3 LDS buffers (3 for tiles of at most 192 rows),
+//     copied by the LDS DMA of global_load_lds one or two K steps ahead and
+//     shared by the 4 waves: they are the MFMA B operand.  Rows are
+//     XOR-swizzled by 16-B chunk so the fragment reads are conflict-free.
 //   * Each wave owns its own weight rows (G1: 32 gate + the matching 32 up
 //     rows; G2: 64 down rows).  It loads their packed codes straight into
 //     registers one K step ahead and dequantizes them in registers into the
@@ -30,11 +45,9 @@
 //     MFMA lane slot holds, as long as both operands agree): lane half h of
 //     every MFMA covers one whole 64-wide NF4 block of its row, so one absmax
 //     and one 16-entry bf16 table serve the lane for the whole K step.  NF4
-//     codes become bf16 through v_perm_b32 byte lookups in that table; within
-//     each group of 8 k the order is evens-first (the order the nibbles come
-//     out of a code byte), and the token rows are written to LDS in the same
-//     order.
-//   * Work items (expert, token tile, column tile) are laid out expert-major
+//     codes become bf16 through v_perm_b32 byte lookups in that table, in
+//     natural k order within each group of 8.
+//   * Work items (expert, column tile, token tile) are laid out expert-major
 //     and dealt to the 8 XCDs in contiguous ranges, so the tiles that share an
 //     expert's weights and token rows run on the same L2.
 #include "moeq_internal.h"
