@@ -92,10 +92,11 @@ def new_events(torch, n):
     return ev
 
 
-def cpu_baseline(s, gu, dn, x, idx, wts, T):
-    """The oracle, untuned, on a bounded sample: NF4 quantize of two experts'
-    gate_up and down, and the forward of T tokens with their expert indices
-    folded onto those two experts (identical work per assignment)."""
+def cpu_baseline(s, gu, dn, x, idx, wts, T, n_quant=32):
+    """The oracle, untuned, on a bounded sample (~10 s of CPU work): NF4
+    quantize of the first `n_quant` experts' gate_up and down, and the forward
+    of all T tokens with their expert indices folded onto experts 0 and 1
+    (identical work per assignment)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -103,28 +104,29 @@ def cpu_baseline(s, gu, dn, x, idx, wts, T):
     from oracle.forward import experts_forward
     from oracle.nf4 import nf4_dequantize, nf4_quantize
 
-    gbits = syn.bf16_bits(gu[:2])
-    dbits = syn.bf16_bits(dn[:2])
+    gbits = syn.bf16_bits(gu[:n_quant])
+    dbits = syn.bf16_bits(dn[:n_quant])
     t0 = time.perf_counter()
     qg = nf4_quantize(gbits)
     qd = nf4_quantize(dbits)
     tq = time.perf_counter() - t0
     qelems = gbits.size + dbits.size
-    dg, dd = nf4_dequantize(*qg), nf4_dequantize(*qd)
-    Ts = min(T, 1024)
-    xs = syn.bf16_bits(x[:Ts])
-    ids = idx[:Ts].cpu().numpy() % 2
-    ws = wts[:Ts].cpu().numpy()
+    del gbits, dbits
+    dg = nf4_dequantize(qg[0][:2], qg[1][:2])
+    dd = nf4_dequantize(qd[0][:2], qd[1][:2])
+    xs = syn.bf16_bits(x)
+    ids = idx.cpu().numpy() % 2
+    ws = wts.cpu().numpy()
     t0 = time.perf_counter()
     experts_forward(xs, ids, ws, dg, dd)
     tf = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
-        "value": Ts / tf, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "value": T / tf, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "quantize_GBps": qelems * NF4_BYTES_PER_ELEM / tq / 1e9,
-        "sample": (f"NF4 quantize of experts 0-1 of gate_up and down ({qelems} elements, {tq:.1f} s); "
-                   f"fp64 forward of the first {Ts} tokens of the T={T} top-{s.K} workload with expert "
-                   f"indices folded onto those two experts ({tf:.1f} s); numpy/BLAS threads={threads}, "
+        "sample": (f"NF4 quantize of experts 0-{n_quant - 1} of gate_up and down ({qelems} elements, "
+                   f"{tq:.1f} s); fp64 forward of all T={T} tokens of the top-{s.K} workload with expert "
+                   f"indices folded onto experts 0 and 1 ({tf:.1f} s); numpy/BLAS threads={threads}, "
                    f"host cpu_count={os.cpu_count()}"),
     }
 

@@ -83,9 +83,14 @@ struct Fmt<MOEQ_FMT_INT8_ROWWISE> {
   static constexpr int kStep = 64;
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -772,13 +777,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     }
 
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
+    // this lane's half of step ks of the token row: K is a multiple of 64,
+    // so the half is wholly in range or wholly past the end (then row start)
     auto load_b = [&](bf16x8 (&xb)[kS], int ks) {
       const int kb = ks * kStep + (kStep / 2) * hh;
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(brow + (kb < K ? kb : 0));
 #pragma unroll
-      for (int s_ = 0; s_ < kS; ++s_) {
-        const int kk = kb + 8 * s_;
-        xb[s_] = *reinterpret_cast<const bf16x8*>(brow + (kk < K ? kk : 0));
-      }
+      for (int s_ = 0; s_ < kS; ++s_) xb[s_] = p[s_];
     };
     // One K step: issue the next step's token fragments, multiply this
     // step's, then refill this step's code registers two steps ahead.  Loads
