@@ -24,6 +24,9 @@ Sources (page title, then section):
   loop as the correctness-first forward).
 * unsloth-zoo issue #850, *Suggested fix*: the experts interface
   ``(hidden_states, top_k_index, top_k_weights)``.
+* Axolotl issue #3787 "Expert-granularity CPU offload for quantized MoE",
+  *Use case*: adapter training steps over frozen 4-bit experts, the
+  workload the backward serves.
 
 Modules:
 
@@ -32,6 +35,8 @@ Modules:
 * :mod:`oracle.int8`    -- row-wise int8 quantize, dequantize.
 * :mod:`oracle.routing` -- per-expert bucketing of top-k assignments.
 * :mod:`oracle.forward` -- the routed experts forward in fp64.
+* :mod:`oracle.backward` -- its gradients with respect to the hidden states
+  and the routing weights (frozen weights), in fp64.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, exact rational arithmetic or library

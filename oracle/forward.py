@@ -49,11 +49,41 @@ def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
     output columns, since output column n depends only on down row n.
     """
     x = bf16_to_f32(hidden_bits).astype(np.float64)
-    idx = np.asarray(top_k_index, dtype=np.int64)
     wts = np.asarray(top_k_weights, dtype=np.float32).astype(np.float64)
+    return experts_forward_f64(x, top_k_index, wts, _Widen(gate_up), _Widen(down),
+                               lambda: H_of(down, x.shape[1]))
+
+
+class _Widen:
+    """Expert -> its bf16 weight widened to fp64, on demand."""
+
+    def __init__(self, w):
+        self.w = w
+
+    def __len__(self):
+        return len(self.w)
+
+    def __getitem__(self, e):
+        return bf16_to_f32(self.w[e]).astype(np.float64)
+
+
+def H_of(down, H):
+    """Output width when nothing is routed: the down rows held per expert."""
+    if isinstance(down, np.ndarray) and down.ndim == 3:
+        return down.shape[1]
+    return down[0].shape[0] if len(down) else H
+
+
+def experts_forward_f64(x, top_k_index, top_k_weights, gate_up, down, n_empty=None):
+    """The same forward on real-valued operands: ``x`` fp64 ``[T, H]``,
+    ``top_k_weights`` ``[T, K]``, ``gate_up[e]`` ``[2I, H]`` and ``down[e]``
+    ``[H', I]`` as fp64 arrays.  ``n_empty``: a callable giving the output
+    width when nothing is routed (default: H)."""
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(top_k_index, dtype=np.int64)
+    wts = np.asarray(top_k_weights, dtype=np.float64)
     T, H = x.shape
     K = idx.shape[1]
-    n_out = None
     y = None
 
     E = len(gate_up)
@@ -61,8 +91,8 @@ def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
         if e < 0 or e >= E:                         # not routed: contributes nothing
             continue
         tok, kk = np.nonzero(idx == e)              # every (t, k) served by expert e
-        w_gu = bf16_to_f32(gate_up[int(e)]).astype(np.float64)   # [2I, H]
-        w_d = bf16_to_f32(down[int(e)]).astype(np.float64)       # [H, I]
+        w_gu = np.asarray(gate_up[int(e)], dtype=np.float64)   # [2I, H]
+        w_d = np.asarray(down[int(e)], dtype=np.float64)       # [H', I]
         I = w_gu.shape[0] // 2
         assert w_gu.shape == (2 * I, H) and w_d.shape[1] == I
         X = x[tok]                                  # [n, H]
@@ -70,15 +100,12 @@ def experts_forward(hidden_bits, top_k_index, top_k_weights, gate_up, down):
         u = X @ w_gu[I:].T                          # up: last I rows
         h = silu(g) * u                             # [n, I]
         if y is None:
-            n_out = w_d.shape[0]
-            y = np.zeros((T, K, n_out), dtype=np.float64)
-        y[tok, kk] = h @ w_d.T                      # [n, n_out]
+            y = np.zeros((T, K, w_d.shape[0]), dtype=np.float64)
+        y[tok, kk] = h @ w_d.T                      # [n, H']
 
     if y is None:                                   # nothing routed
-        n_out = H if isinstance(down, np.ndarray) and down.ndim == 3 and down.shape[1] == H else (
-            down[0].shape[0] if len(down) else H)
-        y = np.zeros((T, K, n_out), dtype=np.float64)
-    out = np.zeros((T, n_out), dtype=np.float64)
+        y = np.zeros((T, K, H if n_empty is None else n_empty()), dtype=np.float64)
+    out = np.zeros((T, y.shape[2]), dtype=np.float64)
     for k in range(K):
         out += wts[:, k:k + 1] * y[:, k]
     return out
