@@ -20,6 +20,7 @@ __all__ = [
     "moeq_quantize_nf4", "moeq_quantize_int8_rowwise", "moeq_dequantize",
     "moeq_experts_forward_workspace_bytes", "moeq_experts_forward",
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
+    "moeq_experts_backward_workspace_bytes", "moeq_experts_backward",
 ]
 
 FMT_NF4 = 1
@@ -70,6 +71,8 @@ def _load():
         "moeq_experts_forward": (I32, [P, P, P, I32, I32, QP, QP, P, P, SZ, P]),
         "moeq_experts_forward_timed": (I32, [P, P, P, I32, I32, QP, QP, P, P, SZ, P, P]),
         "moeq_route_workspace_bytes": (SZ, [I32, I32, I32]),
+        "moeq_experts_backward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
+        "moeq_experts_backward": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, SZ, P]),
         "moeq_route_buckets": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -235,6 +238,45 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
         arr = (ctypes.c_void_p * 5)(*[int(e) for e in stage_events])
         _check(lib.moeq_experts_forward_timed(*args, arr), "moeq_experts_forward_timed")
     return out
+
+
+def moeq_experts_backward_workspace_bytes(T, K, gate_up, down):
+    gu, dn = gate_up._c(), down._c()
+    return int(_load().moeq_experts_backward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
+
+
+def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, grad_out, grad_hidden=None,
+                          grad_weights=None, workspace=None, stream=None):
+    """Gradients of the experts block with respect to ``hidden`` and
+    ``top_k_weights`` (packed weights frozen) for the incoming gradient
+    ``grad_out`` (bf16 ``[T, H]``); returns ``(grad_hidden bf16 [T, H],
+    grad_weights fp32 [T, K])``."""
+    _dev(hidden, torch.bfloat16, "hidden")
+    _dev(top_k_index, torch.int32, "top_k_index")
+    _dev(top_k_weights, torch.float32, "top_k_weights")
+    _dev(grad_out, torch.bfloat16, "grad_out")
+    T, H = hidden.shape
+    K = top_k_index.shape[1]
+    if tuple(top_k_index.shape) != (T, K) or tuple(top_k_weights.shape) != (T, K):
+        raise ValueError("top_k_index and top_k_weights must both be [T, K]")
+    if tuple(grad_out.shape) != (T, H) or H != gate_up.cols:
+        raise ValueError("grad_out must be [T, H] with H = gate_up cols")
+    if grad_hidden is None:
+        grad_hidden = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    if grad_weights is None:
+        grad_weights = torch.empty((T, K), dtype=torch.float32, device=hidden.device)
+    _dev(grad_hidden, torch.bfloat16, "grad_hidden")
+    _dev(grad_weights, torch.float32, "grad_weights")
+    gu, dn = gate_up._c(), down._c()
+    lib = _load()
+    need = int(lib.moeq_experts_backward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    _check(lib.moeq_experts_backward(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
+                                     ctypes.byref(gu), ctypes.byref(dn), _ptr(grad_out), _ptr(grad_hidden),
+                                     _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moeq_experts_backward")
+    return grad_hidden, grad_weights
 
 
 def moeq_route_workspace_bytes(T, K, E):

@@ -195,6 +195,67 @@ moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, co
                                              reinterpret_cast<hipEvent_t const*>(stage_events)));
 }
 
+// Backward workspace: the routing buffers, then h bf16 [n][I], g|u fp32
+// [n][2I], z / dx fp32 [n][H] and dg|du bf16 [n][2I], 256-B aligned.
+struct BwLayout {
+  Layout route;
+  size_t h, gu, zdx, dgu, total;
+};
+BwLayout bw_layout(int64_t n, int32_t E, int64_t I, int64_t H) {
+  BwLayout L;
+  L.route = layout(n, E, 0, 0);
+  size_t o = L.route.total;
+  L.h = o;   o += up(sizeof(uint16_t) * (size_t)(n * I));
+  L.gu = o;  o += up(sizeof(float) * (size_t)(n * 2 * I));
+  L.zdx = o; o += up(sizeof(float) * (size_t)(n * H));
+  L.dgu = o; o += up(sizeof(uint16_t) * (size_t)(n * 2 * I));
+  L.total = o;
+  return L;
+}
+
+moeq_status check_backward_shapes(int32_t T, int32_t K, const moeq_qweight* gu, const moeq_qweight* dn) {
+  moeq_status st = check_forward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  // the transposed GEMMs address rows of dg|du with 32-bit byte offsets
+  if ((int64_t)T * K * gu->rows * 2 >= (int64_t(1) << 32)) return MOEQ_ESHAPE;
+  return MOEQ_OK;
+}
+
+size_t moeq_experts_backward_workspace_bytes(int32_t T, int32_t K, const moeq_qweight* gu,
+                                             const moeq_qweight* dn) {
+  if (check_backward_shapes(T, K, gu, dn) != MOEQ_OK) return 0;
+  return bw_layout((int64_t)T * K, gu->num_experts, gu->rows / 2, gu->cols).total;
+}
+
+moeq_status moeq_experts_backward(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T, int32_t K,
+                                  const moeq_qweight* gu, const moeq_qweight* dn, const uint16_t* dout,
+                                  uint16_t* grad_x, float* grad_w, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  moeq_status st = check_backward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !idx || !wts || !dout || !grad_x || !grad_w) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(dout) || !aligned16(grad_x)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const BwLayout L = bw_layout((int64_t)T * K, E, I, H);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  if (!aligned16(workspace)) return MOEQ_EALIGN;
+  char* w = static_cast<char*>(workspace);
+  BackwardArgs a;
+  a.x = x; a.idx = idx; a.wts = wts; a.dout = dout;
+  a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
+  a.format = gu->format;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales;
+  a.grad_x = grad_x; a.grad_w = grad_w;
+  a.rb = route_buffers(workspace, L.route);
+  a.h = reinterpret_cast<uint16_t*>(w + L.h);
+  a.gu_save = reinterpret_cast<float*>(w + L.gu);
+  a.zdx = reinterpret_cast<float*>(w + L.zdx);
+  a.dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
+  return device_status(launch_experts_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E) {
   if (T < 0 || K < 1 || E < 1 || E > MOEQ_MAX_EXPERTS || (int64_t)T * K > kMaxAssignments) return 0;
   return layout((int64_t)T * K, E, 0, 0).total;

@@ -50,6 +50,8 @@
 //   * Work items (expert, column tile, token tile) are laid out expert-major
 //     and dealt to the 8 XCDs in contiguous ranges, so the tiles that share an
 //     expert's weights and token rows run on the same L2.
+#include <type_traits>
+
 #include "moeq_internal.h"
 
 namespace moeq {
@@ -71,6 +73,9 @@ constexpr int kXcds = 8;
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
 constexpr int kVmcntWait = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+// ... and also until every LDS access of this wave has completed.
+template <int N>
+constexpr int kVmcntLgkmWait = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
 
 template <int FMT>
 struct Fmt;
@@ -481,7 +486,7 @@ template <int FMT, int NB>
 __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32_t* prow, int K, int H, int I,
                                         int jcol, bool wave_on, const uint8_t* gq, const float* gs,
                                         const uint8_t* uq, const float* us, int row0, int nrows,
-                                        uint16_t* __restrict__ h) {
+                                        uint16_t* __restrict__ h, float* __restrict__ gu_save) {
   using C = Core<FMT, NB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t roff[C::kInstr];  // byte offset of each staged x row (token perm[p] / K)
@@ -516,6 +521,16 @@ __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32
       }
       *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
+    if (gu_save) {  // the backward keeps g and u of every sorted row: [n][2I] fp32
+      float* gp = gu_save + (int64_t)(row0 + r) * 2 * I + jcol + 4 * hh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<float4*>(gp + 8 * q) =
+            make_float4(accG[b][4 * q], accG[b][4 * q + 1], accG[b][4 * q + 2], accG[b][4 * q + 3]);
+        *reinterpret_cast<float4*>(gp + I + 8 * q) =
+            make_float4(accU[b][4 * q], accU[b][4 * q + 1], accU[b][4 * q + 2], accU[b][4 * q + 3]);
+      }
+    }
   }
 }
 
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx,
-                                                     uint16_t* __restrict__ h) {
+                                                     uint16_t* __restrict__ h, float* __restrict__ gu_save) {
   __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
 
   int e, mt, ct;
@@ -549,13 +564,13 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
   const float* us = ws + urow * spr;
   const int32_t* prow = perm_idx + row0;
   if (nrows > 192)
-    g1_tile<FMT, 8>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+    g1_tile<FMT, 8>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h, gu_save);
   else if (nrows > 128)
-    g1_tile<FMT, 6>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+    g1_tile<FMT, 6>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h, gu_save);
   else if (nrows > 64)
-    g1_tile<FMT, 4>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+    g1_tile<FMT, 4>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h, gu_save);
   else
-    g1_tile<FMT, 2>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h);
+    g1_tile<FMT, 2>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h, gu_save);
 }
 
 // ---------------------------------------------------------------------------
@@ -615,7 +630,8 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
   int row0, nrows;
   tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
   const int t = threadIdx.x, wave = t >> 6, l32 = t & 31;
-  if (t < kBM) sw[t] = (t < nrows) ? wts[perm_idx[row0 + t]] : 0.0f;
+  // wts == nullptr: unit weights (the backward's unweighted y)
+  if (t < kBM) sw[t] = (t < nrows) ? (wts ? wts[perm_idx[row0 + t]] : 1.0f) : 0.0f;
 
   const int ncol = ct * kG2Rows + 64 * wave;  // H % 64 == 0: a wave is all in or all out
   const bool on = ncol < H;
@@ -933,6 +949,289 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward through the frozen packed experts (gradients with respect to the
+// hidden states and the routing weights; see moeq_experts_backward):
+//   recompute  g, u, h = G1 of the forward (g and u kept in fp32),
+//              z = down h (G2 with unit weights)
+//   BW         grad_w[a] = dout[t] . z[a]
+//   T1         dh = w * down^T dout[t];  dg = dh u s (1 + g (1 - s)),
+//              du = dh g s  -> dgu = bf16 [dg | du]                 (s = sigmoid(g))
+//   T2         dx = gate_up^T dgu  (fp32, one row per sorted assignment)
+//   C1         grad_x[t] = bf16(sum over k in order of dx)
+// T1 and T2 are transposed grouped GEMMs: the contraction runs over the rows
+// of the packed weight while its NF4 blocks run along the output columns.
+//
+// tgemm_kernel: out[p][c] = sum_r W_e[r][c] v_p[r] for the tile (expert e, up
+// to 256 sorted rows p, 128 output columns c), K steps of 64 weight rows.
+// Each K step the workgroup
+//   * dequantizes the W tile [64 r][128 c] into LDS in natural layout (every
+//     thread: one row's 32 columns, which lie in one NF4 block), from codes
+//     it loaded one step earlier;
+//   * copies the token tile [256 rows][64 r] into LDS with the LDS DMA (rows
+//     XOR-swizzled by 16-B chunk);
+// and the MFMA A operand (W^T: 8 consecutive r of one column per lane) is read
+// from the natural layout with ds_read_b64_tr_b16, which hands each lane of a
+// 16-lane group one column of a 4 x 16 block of 16-bit values: lane L of the
+// group points at row L / 4, columns 4 (L % 4) .. +3 of the block, and lane i
+// receives column i of all four rows.
+//   MODE 1: W = down_e (R = H rows, C = I columns); v_p = dout[perm[p] / K];
+//           the epilogue forms dg and du from dh = w_p * acc and the saved g, u.
+//   MODE 2: W = gate_up_e (R = 2I, C = H); v_p = dgu[p]; out = dx fp32.
+// Waves: wave w owns output columns 64 (w & 1) .. +64 (two 32-column MFMA
+// blocks) of token rows 128 (w >> 1) .. +128 (four 32-row blocks).
+// ---------------------------------------------------------------------------
+constexpr int kTcols = 128;               // output columns per tile
+constexpr int kTk = 64;                   // weight rows per K step
+constexpr int kTpitch = 2 * kTcols + 32;  // LDS bytes per dequantized W row (padded)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restrict__ vsrc, int32_t Ktop, int32_t E,
+                                                        int32_t R, int32_t C, const uint8_t* __restrict__ wq,
+                                                        const float* __restrict__ ws,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ tile_start,
+                                                        const int32_t* __restrict__ perm_idx,
+                                                        const float* __restrict__ wts,
+                                                        const float* __restrict__ gu_save, void* __restrict__ out) {
+  // one LDS array: the dequantized W tiles, then the token tiles
+  constexpr int kWBytes = kTk * kTpitch, kVBytes = kBM * kTk * 2;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kWBytes + 2 * kVBytes];
+  __shared__ float sw[kBM];
+  auto sW = [&](int b) { return smem + b * kWBytes; };
+  auto sV = [&](int b) { return smem + 2 * kWBytes + b * kVBytes; };
+
+  int e, mt, ct;
+  if (!decode_work(tile_start, E, (C + kTcols - 1) / kTcols, e, mt, ct)) return;
+  int row0, nrows;
+  tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int c0 = ct * kTcols;
+  if (MODE == 1 && t < kBM) sw[t] = (t < nrows) ? wts[perm_idx[row0 + t]] : 0.0f;
+  const int nks = R / kTk;  // R % 64 == 0
+
+  // W tile loader: thread -> row wr of the step, columns wc .. wc + 31
+  const int wr = t >> 2;
+  const int wc = c0 + 32 * (t & 3);
+  const bool wc_in = wc < C;  // C % 64 == 0: a 32-column quarter is wholly in or out
+  const int wcc = wc_in ? wc : 0;
+  const int64_t cpr = (FMT == MOEQ_FMT_NF4) ? C / 2 : C;
+  const int64_t spr = (FMT == MOEQ_FMT_NF4) ? C / kNf4Block : 1;
+  const uint8_t* wrow = wq + ((int64_t)e * R + wr) * cpr + (FMT == MOEQ_FMT_NF4 ? wcc / 2 : wcc);
+  const float* srow = ws + ((int64_t)e * R + wr) * spr + (FMT == MOEQ_FMT_NF4 ? wcc / kNf4Block : 0);
+  struct WCodes {
+    uint4 a, b;  // NF4: a (32 codes); int8: a, b
+    float s;
+    uint32_t m;  // all ones, or zero for a step or column quarter past the end
+  };
+  // Loads for step ks (past the last step: step 0's addresses).  They are
+  // never behind a branch; a step or columns past the end are zeroed through
+  // the scale when the codes are used (a zero scale makes the weights
+  // exactly zero).
+  auto wfetch = [&](WCodes& c, int ks) {
+    const bool in = ks < nks;
+    const int64_t kr = in ? (int64_t)ks * kTk : 0;
+    const uint4* p = reinterpret_cast<const uint4*>(wrow + kr * cpr);
+    c.a = p[0];
+    if (FMT != MOEQ_FMT_NF4) c.b = p[1];
+    c.s = srow[kr * spr];
+    uint32_t m = (in && wc_in) ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));  // opaque: keeps the select from becoming a branch around the loads
+    c.m = m;
+  };
+  auto wstore = [&](const WCodes& c, int buf) {
+    char* dst = sW(buf) + wr * kTpitch + 64 * (t & 3);
+    const float sc = __uint_as_float(__float_as_uint(c.s) & c.m);
+    if constexpr (FMT == MOEQ_FMT_NF4) {
+      const Nf4Table tb = nf4_table(sc);
+      *reinterpret_cast<bf16x8*>(dst) = nf4_frag(tb, c.a.x);
+      *reinterpret_cast<bf16x8*>(dst + 16) = nf4_frag(tb, c.a.y);
+      *reinterpret_cast<bf16x8*>(dst + 32) = nf4_frag(tb, c.a.z);
+      *reinterpret_cast<bf16x8*>(dst + 48) = nf4_frag(tb, c.a.w);
+    } else {
+      const float ns = -128.0f * sc;
+      *reinterpret_cast<bf16x8*>(dst) = i8_frag(c.a.x, c.a.y, sc, ns);
+      *reinterpret_cast<bf16x8*>(dst + 16) = i8_frag(c.a.z, c.a.w, sc, ns);
+      *reinterpret_cast<bf16x8*>(dst + 32) = i8_frag(c.b.x, c.b.y, sc, ns);
+      *reinterpret_cast<bf16x8*>(dst + 48) = i8_frag(c.b.z, c.b.w, sc, ns);
+    }
+  };
+
+  // token tile loader: instruction i of wave w stages rows 8 (4 i + w) .. +7,
+  // lane l row 8 (4 i + w) + l / 8, LDS slot l % 8 holding chunk slot ^ (row & 7)
+  uint32_t voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (4 * i + wave) + (lane >> 3);
+    const int rr = r < nrows ? r : 0;
+    voff[i] = (MODE == 1) ? (uint32_t)(perm_idx[row0 + rr] / Ktop) * (uint32_t)R * 2u
+                          : (uint32_t)(row0 + rr) * (uint32_t)R * 2u;
+  }
+  const int vchunk = (lane & 7) ^ ((lane >> 3) & 7);
+  const char* vbase = reinterpret_cast<const char*>(vsrc);
+  // The DMA target is passed as a bare LDS address: with the array itself
+  // the compiler would make every later LDS read wait for all DMAs in flight.
+  // The explicit waits before each barrier order them instead.
+  uint32_t vlds = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)sV(0);
+  asm volatile("" : "+s"(vlds));  // opaque, so it is not folded back into a pointer to the array
+  auto vstage = [&](int ks, int buf) {
+    const int kk = (ks < nks ? ks * kTk : 0) + 8 * vchunk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(vbase + voff[i] + 2 * kk,
+                                       (__attribute__((address_space(3))) void*)(size_t)(vlds + buf * kVBytes +
+                                                                                         (8 * (4 * i + wave)) * 128),
+                                       16, 0, 0);
+  };
+
+  // A operand addresses (ds_read_b64_tr_b16): lane L = lane % 16 of group
+  // g = lane / 16 points at row 8 (g / 2) + L / 4 (+ 4 for the second read)
+  // of the 16-row MFMA step, columns cb + 16 (g % 2) + 4 (L % 4)
+  const int g16 = lane >> 4, L16 = lane & 15;
+  const int a_off = (8 * (g16 >> 1) + (L16 >> 2)) * kTpitch + 2 * (16 * (g16 & 1) + 4 * (L16 & 3));
+  const int cw = 64 * (wave & 1);    // wave's first tile column
+  const int tw = 128 * (wave >> 1);  // wave's first tile row
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[m][b] = (f32x16){};
+
+  auto mfma_step = [&](int buf) {
+#pragma unroll
+    for (int s4 = 0; s4 < kTk / 16; ++s4) {
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const char* base = sW(buf) + (16 * s4) * kTpitch + 2 * (cw + 32 * m) + a_off;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 4 * kTpitch));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        af[m] = as_bf16x8(l2.x, l2.y, h2.x, h2.y);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int row = tw + 32 * b + l32;
+        const int slot = (2 * s4 + hh) ^ (row & 7);
+        bf[b] = *reinterpret_cast<const bf16x8*>(sV(buf) + row * 128 + slot * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[m][b] = mfma(af[m], bf[b], acc[m][b]);
+    }
+  };
+
+  // Step ks: stage step ks+1 (token DMA, W dequant from codes loaded a step
+  // ago), load step ks+2's codes, multiply step ks, then wait for this
+  // thread's DMA and meet at the barrier.  Two code register sets in turn.
+  WCodes ca, cb;
+  wfetch(ca, 0);
+  vstage(0, 0);
+  wstore(ca, 0);  // waits for the codes (and the DMA issued before them)
+  wfetch(ca, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // (the buffer index is a compile-time constant in each copy, so the
+  // compiler can tell the DMA's LDS target from the buffer being read)
+  auto kstep = [&](auto bufc, int ks, WCodes& cn, WCodes& cnn) {
+    constexpr int buf = decltype(bufc)::value;
+    __builtin_amdgcn_sched_barrier(0);  // nothing of the next step moves up here (it would wait for its codes)
+    // dequantize step ks + 1's codes (loaded a step ago) before issuing the
+    // DMA, so waiting for the codes does not also wait for the DMA
+    wstore(cn, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    vstage(ks + 1, buf ^ 1);
+    // The code loads must issue after the DMAs: the wait before the barrier
+    // counts on the DMAs being the older loads.
+    __builtin_amdgcn_sched_barrier(0);
+    wfetch(cnn, ks + 2);
+    mfma_step(buf);
+    // The codes just fetched may stay in flight; every earlier load (the
+    // DMA for step ks + 1) has landed, and this wave's LDS writes are done.
+    // A release fence would also wait for the codes (LDS DMA counts as a
+    // vector load), so the barrier is bare, with an acquire fence after it.
+    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<(FMT == MOEQ_FMT_NF4) ? 2 : 3>);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // two steps per trip with no branch between them; for an odd step count
+  // the last trip's second step has zero weights and adds nothing
+  for (int ks = 0; ks < nks; ks += 2) {
+    kstep(std::integral_constant<int, 0>{}, ks, ca, cb);
+    kstep(std::integral_constant<int, 1>{}, ks + 1, cb, ca);
+  }
+
+  // epilogue: lane holds, per column block m and token block b, output
+  // columns cw + 32 m + 8 q + 4 hh + 0..3 of tile row tw + 32 b + l32
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int r = tw + 32 * b + l32;
+    if (r >= nrows) continue;
+    const int64_t p = row0 + r;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + cw + 32 * m + 8 * q + 4 * hh;
+        if (c >= C) continue;
+        const f32x16& a = acc[m][b];
+        if constexpr (MODE == 1) {
+          const float w = sw[r];
+          const float4 g4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + c);
+          const float4 u4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + C + c);
+          const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+          float dg[4], du[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dh = w * a[4 * q + i];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
+            du[i] = dh * gv[i] * sg;
+            dg[i] = dh * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg));
+          }
+          uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
+          *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + p * C + c) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+      }
+    }
+  }
+}
+
+// grad_w[a] = dout[a / K] . z[slot[a]] (0 for an unrouted assignment), one
+// wave per assignment, lanes summed in a fixed tree order.
+__global__ __launch_bounds__(kThreads) void gradw_kernel(const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ z,
+                                                        const int32_t* __restrict__ slot, int32_t n, int32_t K,
+                                                        int32_t H, float* __restrict__ gw) {
+  const int64_t a = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (a >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int p = slot[a];
+  float acc = 0.0f;
+  if (p >= 0) {
+    const uint16_t* d = dout + (a / K) * H;
+    const float* zr = z + (int64_t)p * H;
+    for (int j = 4 * lane; j < H; j += 256) {
+      const uint2 dv = *reinterpret_cast<const uint2*>(d + j);
+      const float4 zv = *reinterpret_cast<const float4*>(zr + j);
+      acc += __uint_as_float(dv.x << 16) * zv.x + __uint_as_float(dv.x & 0xffff0000u) * zv.y +
+             __uint_as_float(dv.y << 16) * zv.z + __uint_as_float(dv.y & 0xffff0000u) * zv.w;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) gw[a] = acc;
+}
+
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 }  // namespace
@@ -993,13 +1292,13 @@ hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   if (a.format == MOEQ_FMT_NF4) {
     g1_kernel<MOEQ_FMT_NF4><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.rb.offsets,
-                                                    a.rb.tile_start, a.rb.perm, a.h);
+                                                    a.rb.tile_start, a.rb.perm, a.h, nullptr);
     if (ev) hipEventRecord(ev[2], s);
     g2_kernel<MOEQ_FMT_NF4><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.rb.offsets,
                                                     a.rb.tile_start, a.rb.perm, a.y);
   } else {
     g1_kernel<MOEQ_FMT_INT8_ROWWISE><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s,
-                                                             a.rb.offsets, a.rb.tile_start, a.rb.perm, a.h);
+                                                             a.rb.offsets, a.rb.tile_start, a.rb.perm, a.h, nullptr);
     if (ev) hipEventRecord(ev[2], s);
     g2_kernel<MOEQ_FMT_INT8_ROWWISE><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s,
                                                              a.rb.offsets, a.rb.tile_start, a.rb.perm, a.y);
@@ -1007,6 +1306,45 @@ hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_
   if (ev) hipEventRecord(ev[3], s);
   combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.rb.slot, a.K, a.H, a.out);
   if (ev) hipEventRecord(ev[4], s);
+  return hipGetLastError();
+}
+
+hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s) {
+  const int32_t n = a.T * a.K;
+  hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
+  if (err != hipSuccess) return err;
+  const int mtiles = (n + kBM - 1) / kBM + a.E;
+  const int g1 = round_up(mtiles * ((a.I + kG1Cols - 1) / kG1Cols), kXcds);
+  const int g2 = round_up(mtiles * ((a.H + kG2Rows - 1) / kG2Rows), kXcds);
+  const int t1 = round_up(mtiles * ((a.I + kTcols - 1) / kTcols), kXcds);
+  const int t2 = round_up(mtiles * ((a.H + kTcols - 1) / kTcols), kXcds);
+  const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
+  const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
+  const RouteBuffers& r = a.rb;
+  if (a.format == MOEQ_FMT_NF4) {
+    g1_kernel<MOEQ_FMT_NF4><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, r.offsets, r.tile_start,
+                                                    r.perm, a.h, a.gu_save);
+    g2_kernel<MOEQ_FMT_NF4><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
+                                                    r.tile_start, r.perm, a.zdx);
+    gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
+    tgemm_kernel<MOEQ_FMT_NF4, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
+                                                          r.tile_start, r.perm, a.wts, a.gu_save, a.dgu);
+    tgemm_kernel<MOEQ_FMT_NF4, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s, r.offsets,
+                                                          r.tile_start, r.perm, nullptr, nullptr, a.zdx);
+  } else {
+    g1_kernel<MOEQ_FMT_INT8_ROWWISE><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, r.offsets,
+                                                             r.tile_start, r.perm, a.h, a.gu_save);
+    g2_kernel<MOEQ_FMT_INT8_ROWWISE><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
+                                                             r.tile_start, r.perm, a.zdx);
+    gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
+    tgemm_kernel<MOEQ_FMT_INT8_ROWWISE, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s,
+                                                                   r.offsets, r.tile_start, r.perm, a.wts,
+                                                                   a.gu_save, a.dgu);
+    tgemm_kernel<MOEQ_FMT_INT8_ROWWISE, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s,
+                                                                   r.offsets, r.tile_start, r.perm, nullptr,
+                                                                   nullptr, a.zdx);
+  }
+  combine_kernel<<<a.T, kThreads, 0, s>>>(a.zdx, r.slot, a.K, a.H, a.grad_x);
   return hipGetLastError();
 }
 

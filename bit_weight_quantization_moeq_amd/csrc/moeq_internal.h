@@ -90,6 +90,27 @@ struct ForwardArgs {
 };
 // events: NULL or 5 events recorded at the stage boundaries.
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
+
+struct BackwardArgs {
+  const uint16_t* x;        // [T][H]
+  const int32_t* idx;       // [T][K]
+  const float* wts;         // [T][K]
+  const uint16_t* dout;     // [T][H]
+  int32_t T, K, E, H, I;
+  int32_t format;
+  const void* gu_q;
+  const float* gu_s;
+  const void* dn_q;
+  const float* dn_s;
+  uint16_t* grad_x;         // [T][H]
+  float* grad_w;            // [T][K]
+  RouteBuffers rb;
+  uint16_t* h;              // [n][I] bf16, sorted rows
+  float* gu_save;           // [n][2I] fp32, sorted rows
+  float* zdx;               // [n][H] fp32, sorted rows: z, then dx
+  uint16_t* dgu;            // [n][2I] bf16, sorted rows
+};
+hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s);
 int32_t forward_tile_rows();
 
 }  // namespace moeq

@@ -176,6 +176,35 @@ moeq_status moeq_experts_forward_timed(const uint16_t *hidden_bf16, const int32_
                                        void *stream, void *const *stage_events);
 
 /*
+ * Gradients of the routed experts block with respect to its inputs, the
+ * packed weights frozen: the workload the quantized experts serve is adapter
+ * training over frozen 4-bit/8-bit experts ("MoE Expert Quantization",
+ * Axolotl docs, intro and Expert LoRA targeting; Axolotl issue #3787, Use
+ * case).  With out = moeq_experts_forward(...) and the incoming gradient
+ * grad_out = dL/dout (bf16 [T][H]):
+ *   grad_hidden_bf16   bf16 [T][H]: dL/dhidden = sum_k (gate^T dg + up^T du),
+ *                      added in k order, with dh = w * down^T grad_out_t,
+ *                      dg = dh u s (1 + g (1 - s)), du = dh g s,
+ *                      s = sigmoid(g), g / u the gate / up projections
+ *   grad_weights       fp32 [T][K]: dL/dw[t,k] = grad_out_t . (down h);
+ *                      0 for an unrouted assignment
+ * Same arguments and rules as moeq_experts_forward otherwise; the forward's
+ * gate_up GEMM is recomputed inside (g, u and h are not taken from a previous
+ * call).  Roundings: h and dg/du feed bf16 MFMA operands; every sum is fp32;
+ * deterministic (no float atomics).  workspace: at least
+ * moeq_experts_backward_workspace_bytes(T, K, gate_up, down) bytes.
+ * MOEQ_ESHAPE additionally unless T*K*2I*2 bytes < 4 GiB.
+ */
+size_t moeq_experts_backward_workspace_bytes(int32_t T, int32_t K, const moeq_qweight *gate_up,
+                                             const moeq_qweight *down);
+moeq_status moeq_experts_backward(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                  const float *top_k_weights, int32_t T, int32_t K,
+                                  const moeq_qweight *gate_up, const moeq_qweight *down,
+                                  const uint16_t *grad_out_bf16, uint16_t *grad_hidden_bf16,
+                                  float *grad_weights, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/*
  * The routing stage of moeq_experts_forward on its own (same kernels):
  * groups the T*K assignments a = t*K + k by expert (unsloth-zoo issue #850,
  * Suggested fix: one generic routing for every architecture).

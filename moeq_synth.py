@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-GATE_UP, DOWN, HIDDEN, CHOICE, LOGITS, OUTLIERS = range(6)
+GATE_UP, DOWN, HIDDEN, CHOICE, LOGITS, OUTLIERS, GRAD_OUT = range(7)
 
 
 @dataclass(frozen=True)
@@ -115,6 +115,13 @@ def hidden_states(T, H, *, seed=0, layer=0, device="cpu"):
     rng = _rng(seed, layer, HIDDEN)
     x = torch.from_numpy(rng.standard_normal(T * H, dtype=np.float32)).to(torch.bfloat16)
     return x.reshape(T, H).to(device)
+
+
+def grad_output(T, H, *, seed=0, layer=0, device="cpu"):
+    """bf16 ``[T, H]`` ~ N(0, 1): an incoming gradient for the backward."""
+    rng = _rng(seed, layer, GRAD_OUT)
+    g = torch.from_numpy(rng.standard_normal(T * H, dtype=np.float32)).to(torch.bfloat16)
+    return g.reshape(T, H).to(device)
 
 
 def routing(T, K, E, *, kind="uniform", zipf_s=1.1, seed=0, layer=0, device="cpu"):
