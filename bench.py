@@ -14,7 +14,8 @@ around the forward of the timed steps that record no stage events),
 kernel of the step, from the stage events recorded on every other timed step;
 ``device_copy_GBps`` = a plain 1 GiB device copy, the measured HBM ceiling;
 ``decode`` = forward-only figures at T = 1 and 32, streaming the weights from
-HBM; ``codec`` = row-wise int8 quantize and the two dequantizes;
+HBM; ``backward`` = the gradients through the frozen packed experts for the
+same batch; ``codec`` = row-wise int8 quantize and the two dequantizes;
 ``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-codec", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     return ap.parse_args()
 
 
@@ -192,6 +194,33 @@ def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, ca
                          "touched_experts": Ud, "stage_ms_with_events": kms,
                          "timing": f"{calls} back-to-back calls over {layers} layer copies"}
     return dec
+
+
+def backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev, reps=10):
+    """Gradients of the experts block (hidden states and routing weights, the
+    packed weights frozen) for the same layer and batch: events around
+    back-to-back calls.  Work: the gate_up GEMM recomputed (4 T K H I flops),
+    the unweighted down GEMM (2), the down^T GEMM (2) and the gate_up^T GEMM
+    (4): 12 T K H I flops."""
+    T = x.shape[0]
+    dout = syn.grad_output(T, s.H, device=dev)
+    ws = torch.empty(moeq.moeq_experts_backward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+    gx = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((T, s.K), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout, grad_hidden=gx, grad_weights=gw, workspace=ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout, grad_hidden=gx, grad_weights=gw, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 12.0 * T * s.K * s.H * s.I
+    return {"workload": f"same layer and batch (T={T}), incoming gradient ~ N(0, 1) bf16",
+            "ms": ms, "tokens_per_s": T / (ms * 1e-3), "TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "flops": "12 T K H I (gate_up recompute 4, unweighted down 2, down^T 2, gate_up^T 4)"}
 
 
 def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
@@ -372,6 +401,8 @@ def main():
 
     if not args.no_decode:
         result["decode"] = decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps)
+    if not args.no_backward:
+        result["backward"] = backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev)
     if not args.no_codec:
         result["codec"] = codec_figures(torch, np, moeq, syn, dev, copy_GBps)
 
