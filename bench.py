@@ -15,7 +15,8 @@ kernel of the step, from the stage events recorded on every other timed step;
 ``device_copy_GBps`` = a plain 1 GiB device copy, the measured HBM ceiling;
 ``decode`` = forward-only figures at T = 1 and 32, streaming the weights from
 HBM; ``backward`` = the gradients through the frozen packed experts for the
-same batch; ``codec`` = row-wise int8 quantize and the two dequantizes;
+same batch; ``router`` = the router front-end (gate GEMM, softmax, top-K)
+on the same batch; ``codec`` = row-wise int8 quantize and the two dequantizes;
 ``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
@@ -48,6 +49,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-codec", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-router", action="store_true")
     return ap.parse_args()
 
 
@@ -221,6 +223,28 @@ def backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev, reps=10)
             "ms": ms, "tokens_per_s": T / (ms * 1e-3), "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "flops": "12 T K H I (gate_up recompute 4, unweighted down 2, down^T 2, gate_up^T 4)"}
+
+
+def router_figures(torch, np, moeq, syn, s, x, dev, copy_GBps, reps=20):
+    """Router front-end on the benchmark batch: a bf16 gate [E, H] -> top-K
+    indices and weights.  HBM-bound: the hidden states are read once
+    (T H 2 B), the gate once, the outputs written once (8 T K B)."""
+    T = x.shape[0]
+    gate = syn.router_weight(s.E, s.H, device=dev)
+    idx = torch.empty((T, s.K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, s.K), dtype=torch.float32, device=dev)
+    moeq.moeq_router_topk(x, gate, s.K, top_k_index=idx, top_k_weights=w)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        moeq.moeq_router_topk(x, gate, s.K, top_k_index=idx, top_k_weights=w)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 2.0 * T * s.H + 2.0 * s.E * s.H + 8.0 * T * s.K
+    return {"workload": f"T={T}, gate [{s.E}, {s.H}] bf16, top-{s.K}", "ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "TFLOPs": 2.0 * T * s.E * s.H / (ms * 1e-3) / 1e12}
 
 
 def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
@@ -401,6 +425,8 @@ def main():
 
     if not args.no_decode:
         result["decode"] = decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps)
+    if not args.no_router:
+        result["router"] = router_figures(torch, np, moeq, syn, s, x, dev, copy_GBps)
     if not args.no_backward:
         result["backward"] = backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev)
     if not args.no_codec:

@@ -20,7 +20,7 @@ __all__ = [
     "moeq_quantize_nf4", "moeq_quantize_int8_rowwise", "moeq_dequantize",
     "moeq_experts_forward_workspace_bytes", "moeq_experts_forward",
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
-    "moeq_experts_backward_workspace_bytes", "moeq_experts_backward",
+    "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
 ]
 
 FMT_NF4 = 1
@@ -73,6 +73,7 @@ def _load():
         "moeq_route_workspace_bytes": (SZ, [I32, I32, I32]),
         "moeq_experts_backward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
         "moeq_experts_backward": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, SZ, P]),
+        "moeq_router_topk": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P]),
         "moeq_route_buckets": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -277,6 +278,27 @@ def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, gra
                                      _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream)),
            "moeq_experts_backward")
     return grad_hidden, grad_weights
+
+
+def moeq_router_topk(hidden, gate, K, renormalize=False, top_k_index=None, top_k_weights=None, stream=None):
+    """Router front-end: ``hidden`` bf16 ``[T, H]``, ``gate`` bf16 ``[E, H]`` ->
+    ``(top_k_index int32 [T, K], top_k_weights fp32 [T, K])``."""
+    _dev(hidden, torch.bfloat16, "hidden")
+    _dev(gate, torch.bfloat16, "gate")
+    T, H = hidden.shape
+    E = gate.shape[0]
+    if gate.dim() != 2 or gate.shape[1] != H:
+        raise ValueError("gate must be [E, H]")
+    if top_k_index is None:
+        top_k_index = torch.empty((T, int(K)), dtype=torch.int32, device=hidden.device)
+    if top_k_weights is None:
+        top_k_weights = torch.empty((T, int(K)), dtype=torch.float32, device=hidden.device)
+    _dev(top_k_index, torch.int32, "top_k_index")
+    _dev(top_k_weights, torch.float32, "top_k_weights")
+    _check(_load().moeq_router_topk(_ptr(hidden), _ptr(gate), int(T), int(H), int(E), int(K),
+                                    1 if renormalize else 0, _ptr(top_k_index), _ptr(top_k_weights),
+                                    _stream(stream)), "moeq_router_topk")
+    return top_k_index, top_k_weights
 
 
 def moeq_route_workspace_bytes(T, K, E):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoeq.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "quant.hip", "route.hip", "experts.hip"]
+SOURCES = ["api.hip", "quant.hip", "route.hip", "experts.hip", "router.hip"]
 ARCH = "gfx950"
 
 # IEEE fp32 division and denormals stay on (no fast-math, no FTZ): the NF4 and

@@ -256,6 +256,18 @@ moeq_status moeq_experts_backward(const uint16_t* x, const int32_t* idx, const f
   return device_status(launch_experts_backward(a, static_cast<hipStream_t>(stream)));
 }
 
+moeq_status moeq_router_topk(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
+                             int32_t renormalize, int32_t* idx, float* wts, void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || K < 1) return MOEQ_EINVAL;
+  if (H % 64 != 0 || K > E || E > MOEQ_MAX_EXPERTS) return MOEQ_ESHAPE;
+  if ((int64_t)T * H * 2 >= (int64_t(1) << 40)) return MOEQ_ESHAPE;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !gate || !idx || !wts) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(gate)) return MOEQ_EALIGN;
+  return device_status(launch_router(x, gate, T, H, E, K, renormalize ? 1 : 0, idx, wts,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E) {
   if (T < 0 || K < 1 || E < 1 || E > MOEQ_MAX_EXPERTS || (int64_t)T * K > kMaxAssignments) return 0;
   return layout((int64_t)T * K, E, 0, 0).total;

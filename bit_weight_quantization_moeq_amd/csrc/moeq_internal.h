@@ -111,6 +111,9 @@ struct BackwardArgs {
   uint16_t* dgu;            // [n][2I] bf16, sorted rows
 };
 hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s);
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
+                         int32_t renorm, int32_t* idx, float* wts, hipStream_t s);
 int32_t forward_tile_rows();
 
 }  // namespace moeq

@@ -205,6 +205,28 @@ moeq_status moeq_experts_backward(const uint16_t *hidden_bf16, const int32_t *to
                                   void *stream);
 
 /*
+ * Router front-end producing the experts' (top_k_index, top_k_weights): the
+ * gate weight mlp.gate.weight stays bf16 beside the quantized experts
+ * ("MoE Expert Quantization", Axolotl docs, Expert LoRA targeting;
+ * bitsandbytes issue #1849, maintainer thread: router-only training over
+ * NF4 experts) and feeds the uniform experts interface (unsloth-zoo issue
+ * #850, Suggested fix).
+ *   hidden_bf16    bf16 [T][H], 16-byte aligned
+ *   gate_bf16      bf16 [E][H] (one row per expert), 16-byte aligned
+ *   logits         gate @ x_t: bf16 operands, fp32 accumulation
+ *   top_k_index    int32 [T][K]: the K largest logits, largest first, equal
+ *                  logits to the lower expert index
+ *   top_k_weights  fp32 [T][K]: softmax over all E of the selected logits;
+ *                  with renormalize != 0 divided by their sum (a softmax
+ *                  over the K selected logits)
+ * Deterministic.  MOEQ_ESHAPE unless H % 64 == 0 and 1 <= K <= E <=
+ * MOEQ_MAX_EXPERTS; T == 0 is a valid no-op.
+ */
+moeq_status moeq_router_topk(const uint16_t *hidden_bf16, const uint16_t *gate_bf16, int32_t T, int32_t H,
+                             int32_t E, int32_t K, int32_t renormalize, int32_t *top_k_index,
+                             float *top_k_weights, void *stream);
+
+/*
  * The routing stage of moeq_experts_forward on its own (same kernels):
  * groups the T*K assignments a = t*K + k by expert (unsloth-zoo issue #850,
  * Suggested fix: one generic routing for every architecture).

@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-GATE_UP, DOWN, HIDDEN, CHOICE, LOGITS, OUTLIERS, GRAD_OUT = range(7)
+GATE_UP, DOWN, HIDDEN, CHOICE, LOGITS, OUTLIERS, GRAD_OUT, ROUTER = range(8)
 
 
 @dataclass(frozen=True)
@@ -115,6 +115,13 @@ def hidden_states(T, H, *, seed=0, layer=0, device="cpu"):
     rng = _rng(seed, layer, HIDDEN)
     x = torch.from_numpy(rng.standard_normal(T * H, dtype=np.float32)).to(torch.bfloat16)
     return x.reshape(T, H).to(device)
+
+
+def router_weight(E, H, *, std=0.02, seed=0, layer=0, device="cpu"):
+    """bf16 ``[E, H]`` ~ N(0, std^2): a router (gate) weight."""
+    rng = _rng(seed, layer, ROUTER)
+    g = torch.from_numpy(rng.standard_normal(E * H, dtype=np.float32) * np.float32(std)).to(torch.bfloat16)
+    return g.reshape(E, H).to(device)
 
 
 def grad_output(T, H, *, seed=0, layer=0, device="cpu"):
