@@ -16,7 +16,8 @@ kernel of the step, from the stage events recorded on every other timed step;
 ``decode`` = forward-only figures at T = 1 and 32, streaming the weights from
 HBM; ``backward`` = the gradients through the frozen packed experts for the
 same batch; ``router`` = the router front-end (gate GEMM, softmax, top-K)
-on the same batch; ``codec`` = row-wise int8 quantize and the two dequantizes;
+on the same batch; ``offload`` = the forward with the packed experts in
+pinned host memory and the next layer prefetched; ``codec`` = row-wise int8 quantize and the two dequantizes;
 ``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
@@ -50,6 +51,7 @@ def parse():
     ap.add_argument("--no-codec", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--no-offload", action="store_true")
     return ap.parse_args()
 
 
@@ -247,6 +249,48 @@ def router_figures(torch, np, moeq, syn, s, x, dev, copy_GBps, reps=20):
             "TFLOPs": 2.0 * T * s.E * s.H / (ms * 1e-3) / 1e12}
 
 
+def offload_figures(torch, np, moeq, s, qg, qd, x, idx, wts, dev, fwd_ms, layers=4, passes=2):
+    """Expert-granularity offload: `layers` copies of the benchmark layer in
+    pinned host memory, two device slots, layer N+1 prefetched on a side
+    stream during layer N's forward.  Reported per layer: the resident
+    forward, the host-to-device copy alone, and the offloaded forward in
+    steady state; `overlap` = (resident + copy - offloaded) / min(resident,
+    copy), 1 when the shorter of the two is fully hidden."""
+    from bit_weight_quantization_moeq_amd.offload import ExpertOffload
+    off = ExpertOffload([(qg, qd)] * layers, dev)
+    out = torch.empty((x.shape[0], s.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(x.shape[0], s.K, qg, qd), dtype=torch.uint8,
+                     device=dev)
+    # the copy alone (side stream)
+    hg, hd = off.host[1]
+    dg, dd = off.slots[1]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(off.copy_stream):
+        a.record()
+        for _ in range(3):
+            moeq.moeq_qweight_copy_async(hg, dg)
+            moeq.moeq_qweight_copy_async(hd, dd)
+        b.record()
+    torch.cuda.synchronize()
+    copy_ms = a.elapsed_time(b) / 3
+    off.filled = [None, None]
+    for layer in range(layers):                      # warm
+        off.forward(layer, x, idx, wts, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(passes):
+        for layer in range(layers):
+            off.forward(layer, x, idx, wts, out=out, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    off_ms = a.elapsed_time(b) / (passes * layers)
+    nbytes = off.layer_bytes(0)
+    return {"workload": f"{layers} copies of the benchmark layer in pinned host memory, T={x.shape[0]}",
+            "layer_bytes": nbytes, "copy_ms": copy_ms, "copy_GBps": nbytes / (copy_ms * 1e-3) / 1e9,
+            "resident_forward_ms": fwd_ms, "offloaded_forward_ms": off_ms,
+            "overlap": (fwd_ms + copy_ms - off_ms) / min(fwd_ms, copy_ms)}
+
+
 def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
     """Row-wise int8 quantize on the gpt-oss-shaped experts and dequantize of
     both formats: algorithmic bytes / event time."""
@@ -425,6 +469,8 @@ def main():
 
     if not args.no_decode:
         result["decode"] = decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps)
+    if not args.no_offload:
+        result["offload"] = offload_figures(torch, np, moeq, s, qg, qd, x, idx, wts, dev, fwd)
     if not args.no_router:
         result["router"] = router_figures(torch, np, moeq, syn, s, x, dev, copy_GBps)
     if not args.no_backward:

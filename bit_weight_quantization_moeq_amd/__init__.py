@@ -21,6 +21,7 @@ __all__ = [
     "moeq_experts_forward_workspace_bytes", "moeq_experts_forward",
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
     "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
+    "moeq_qweight_copy_async",
 ]
 
 FMT_NF4 = 1
@@ -74,6 +75,7 @@ def _load():
         "moeq_experts_backward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
         "moeq_experts_backward": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, SZ, P]),
         "moeq_router_topk": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P]),
+        "moeq_qweight_copy_async": (I32, [QP, QP, P]),
         "moeq_route_buckets": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -147,6 +149,13 @@ class QWeight:
     def expert(self, e):
         """Expert ``e`` alone (E = 1), sharing storage."""
         return QWeight(self.format, 1, self.rows, self.cols, self.qdata[e:e + 1], self.scales[e:e + 1])
+
+    def like(self, device, pin_memory=False):
+        """An empty QWeight of the same format and shape on ``device`` (host
+        tensors pinned when ``pin_memory``)."""
+        q = torch.empty(self.qdata.shape, dtype=self.qdata.dtype, device=device, pin_memory=pin_memory)
+        s = torch.empty(self.scales.shape, dtype=self.scales.dtype, device=device, pin_memory=pin_memory)
+        return QWeight(self.format, self.num_experts, self.rows, self.cols, q, s)
 
     def _c(self):
         return _QW(self.format, self.num_experts, self.rows, self.cols, self.blocksize,
@@ -299,6 +308,19 @@ def moeq_router_topk(hidden, gate, K, renormalize=False, top_k_index=None, top_k
                                     1 if renormalize else 0, _ptr(top_k_index), _ptr(top_k_weights),
                                     _stream(stream)), "moeq_router_topk")
     return top_k_index, top_k_weights
+
+
+def moeq_qweight_copy_async(src, dst, stream=None):
+    """Asynchronous copy of a packed tensor between pinned host and device
+    memory (either direction) on ``stream`` (default: torch's current)."""
+    if src.qdata.device.type == "cpu" and not src.qdata.is_pinned():
+        raise ValueError("host source must be pinned")
+    if dst.qdata.device.type == "cpu" and not dst.qdata.is_pinned():
+        raise ValueError("host destination must be pinned")
+    s, d = src._c(), dst._c()
+    _check(_load().moeq_qweight_copy_async(ctypes.byref(s), ctypes.byref(d), _stream(stream)),
+           "moeq_qweight_copy_async")
+    return dst
 
 
 def moeq_route_workspace_bytes(T, K, E):

@@ -268,6 +268,23 @@ moeq_status moeq_router_topk(const uint16_t* x, const uint16_t* gate, int32_t T,
                                      static_cast<hipStream_t>(stream)));
 }
 
+moeq_status moeq_qweight_copy_async(const moeq_qweight* src, const moeq_qweight* dst, void* stream) {
+  moeq_status st = check_qweight(src, 0);
+  if (st != MOEQ_OK) return st;
+  st = check_qweight(dst, src->format);
+  if (st != MOEQ_OK) return st;
+  if (src->num_experts != dst->num_experts || src->rows != dst->rows || src->cols != dst->cols)
+    return MOEQ_ESHAPE;
+  const int64_t n = numel(src);
+  const size_t code_bytes = (size_t)(src->format == MOEQ_FMT_NF4 ? n / 2 : n);
+  const size_t scale_bytes =
+      sizeof(float) * (size_t)(src->format == MOEQ_FMT_NF4 ? n / kNf4Block : (int64_t)src->num_experts * src->rows);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst->qdata, src->qdata, code_bytes, hipMemcpyDefault, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst->scales, src->scales, scale_bytes, hipMemcpyDefault, s);
+  return device_status(e);
+}
+
 size_t moeq_route_workspace_bytes(int32_t T, int32_t K, int32_t E) {
   if (T < 0 || K < 1 || E < 1 || E > MOEQ_MAX_EXPERTS || (int64_t)T * K > kMaxAssignments) return 0;
   return layout((int64_t)T * K, E, 0, 0).total;

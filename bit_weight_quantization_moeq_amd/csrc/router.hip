@@ -37,40 +37,69 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 template <int RBW>  // expert blocks of 32 per wave
 __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ gate, int32_t T, int32_t H,
-                                                         int32_t E, int32_t K, int32_t renorm,
+                                                         int32_t E, int32_t K, int32_t renorm, int32_t P,
                                                          int32_t* __restrict__ idx, float* __restrict__ wts) {
-  extern __shared__ float slog[];  // [kTok][E]
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  extern __shared__ float slog[];  // [P][kTok][E]: partial logits of the P parts of H
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  // waves = (expert block groups) x (P parts of H): wave w takes part w % P
+  // of H for the expert blocks w / P, w / P + 4 / P, ...
+  const int part = wave % P, g0 = wave / P, gstep = kWaves / P;
+  const int hlen = H / P, h0 = part * hlen;  // H % (64 P) == 0
+  const int n64 = hlen / 64;                 // trips of 64 k
 
-  // B operand: token row t0 + l32 (zero for l32 >= 16 or past T)
+  // B operand: token row t0 + l32; A operands: gate rows e = 32 (g0 + gstep
+  // j) + l32.  Rows past the tokens (l32 >= 16, or past T) or past the
+  // experts read row 0 instead: their logits land in columns or rows never
+  // stored.
   const bool tok_on = l32 < kTok && t0 + l32 < T;
-  const uint16_t* xr = x + (tok_on ? (t0 + l32) : 0) * (int64_t)H + 8 * hh;
-  // A operands: gate rows e = 32 (wave + 4 j) + l32
+  const uint16_t* xr = x + (tok_on ? (t0 + l32) : 0) * (int64_t)H + h0 + 8 * hh;
   const uint16_t* gr[RBW];
-  bool g_on[RBW];
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
-    const int e = 32 * (wave + kWaves * j) + l32;
-    g_on[j] = e < E;
-    gr[j] = gate + (int64_t)(g_on[j] ? e : 0) * H + 8 * hh;
+    const int e = 32 * (g0 + gstep * j) + l32;
+    gr[j] = gate + (int64_t)(e < E ? e : 0) * H + h0 + 8 * hh;
   }
   f32x16 acc[RBW];
 #pragma unroll
   for (int j = 0; j < RBW; ++j) acc[j] = (f32x16){};
-  const bf16x8 zero = (bf16x8){};
-  for (int k = 0; k < H; k += 16) {
-    bf16x8 b = ld8(xr + k);
-    b = tok_on ? b : zero;
+  // two trips of 64 k in flight: the loads of trip i+1 issue before trip i's
+  // MFMAs (register sets used in turn)
+  struct Frags {
+    bf16x8 b[4], a[4][RBW];
+  };
+  auto load = [&](Frags& f, int trip) {
+    const int kc = trip < n64 ? 64 * trip : 0;
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      bf16x8 a = ld8(gr[j] + k);
-      a = g_on[j] ? a : zero;
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      f.b[u] = ld8(xr + kc + 16 * u);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) f.a[u][j] = ld8(gr[j] + kc + 16 * u);
     }
+  };
+  auto mul = [&](const Frags& f) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[u][j], f.b[u], acc[j], 0, 0, 0);
+  };
+  Frags fa, fb;
+  load(fa, 0);
+  int i = 0;
+  for (; i + 1 < n64; i += 2) {  // no branch between the two trips
+    load(fb, i + 1);
+    __builtin_amdgcn_sched_barrier(0);  // the next trip's loads issue before this trip's MFMAs
+    mul(fa);
+    __builtin_amdgcn_sched_barrier(0);
+    load(fa, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(fb);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // lane holds logits of experts 32 (wave + 4 j) + 8 q + 4 hh + i for token l32
+  if (i < n64) mul(fa);  // odd trip count: the last trip, already loaded
+  // lane holds partial logits of experts 32 (g0 + gstep j) + 8 q + 4 hh + i for token l32
   if (l32 < kTok) {
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
@@ -78,12 +107,20 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 32 * (wave + kWaves * j) + 8 * q + 4 * hh + i;
-          if (e < E) slog[l32 * E + e] = acc[j][4 * q + i];
+          const int e = 32 * (g0 + gstep * j) + 8 * q + 4 * hh + i;
+          if (e < E) slog[(part * kTok + l32) * E + e] = acc[j][4 * q + i];
         }
     }
   }
   __syncthreads();
+  if (P > 1) {  // add the parts in part order into part 0
+    for (int i = t; i < kTok * E; i += kThreads) {
+      float v = slog[i];
+      for (int p = 1; p < P; ++p) v += slog[p * kTok * E + i];
+      slog[i] = v;
+    }
+    __syncthreads();
+  }
 
   // softmax and top-K: wave w takes tokens w, w + 4, w + 8, w + 12
   constexpr int kPer = (MOEQ_MAX_EXPERTS + 63) / 64;  // logits per lane (at most)
@@ -158,16 +195,20 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
 hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
                          int32_t renorm, int32_t* idx, float* wts, hipStream_t s) {
   const int grid = (T + kTok - 1) / kTok;
-  const size_t lds = sizeof(float) * kTok * (size_t)E;
-  const int rbw = (E + 32 * kWaves - 1) / (32 * kWaves);  // expert blocks per wave
+  const int nrb = (E + 31) / 32;  // expert blocks of 32
+  // few expert blocks: split H across the waves instead (P parts, H % 64P == 0)
+  int P = nrb >= kWaves ? 1 : (nrb >= 2 ? 2 : 4);
+  while (P > 1 && H % (64 * P) != 0) P /= 2;
+  const int rbw = (nrb * P + kWaves - 1) / kWaves;  // expert blocks per wave
+  const size_t lds = sizeof(float) * kTok * (size_t)E * P;
   if (rbw <= 1)
-    router_kernel<1><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, idx, wts);
+    router_kernel<1><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
   else if (rbw <= 2)
-    router_kernel<2><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, idx, wts);
+    router_kernel<2><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
   else if (rbw <= 4)
-    router_kernel<4><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, idx, wts);
+    router_kernel<4><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
   else
-    router_kernel<8><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, idx, wts);
+    router_kernel<8><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
   return hipGetLastError();
 }
 

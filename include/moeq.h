@@ -227,6 +227,20 @@ moeq_status moeq_router_topk(const uint16_t *hidden_bf16, const uint16_t *gate_b
                              float *top_k_weights, void *stream);
 
 /*
+ * Asynchronous copy of one packed expert tensor (codes and scales) between
+ * host and device memory, in either direction, on `stream`: the building
+ * block of expert-granularity offload, where every layer's packed experts
+ * live in pinned host memory, one layer is resident and layer N+1 is
+ * prefetched on a side stream during layer N (Axolotl issue #3787, Proposed
+ * shape; Evidence: the forward is bit-identical with offload on or off).
+ * src and dst must describe the same format and shape; their pointers may be
+ * pinned host memory (allocated pinned, e.g. hipHostMalloc) or device
+ * memory.  The copy is ordered on `stream` like any other call; the caller
+ * makes the compute stream wait (an event) before using dst.
+ */
+moeq_status moeq_qweight_copy_async(const moeq_qweight *src, const moeq_qweight *dst, void *stream);
+
+/*
  * The routing stage of moeq_experts_forward on its own (same kernels):
  * groups the T*K assignments a = t*K + k by expert (unsloth-zoo issue #850,
  * Suggested fix: one generic routing for every architecture).
