@@ -37,6 +37,8 @@ Modules:
 * :mod:`oracle.forward` -- the routed experts forward in fp64.
 * :mod:`oracle.backward` -- its gradients with respect to the hidden states
   and the routing weights (frozen weights), in fp64.
+* :mod:`oracle.dq`      -- double quantization of the NF4 absmax (8-bit codes
+  per 256-block group of one expert, fp32 group scales).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, exact rational arithmetic or library
