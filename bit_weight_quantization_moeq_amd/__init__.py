@@ -21,13 +21,15 @@ __all__ = [
     "moeq_experts_forward_workspace_bytes", "moeq_experts_forward",
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
     "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
-    "moeq_qweight_copy_async",
+    "moeq_qweight_copy_async", "FMT_NF4_DQ", "DQ_GROUP", "moeq_compress_absmax",
 ]
 
 FMT_NF4 = 1
 FMT_INT8_ROWWISE = 2
+FMT_NF4_DQ = 3
 NF4_BLOCKSIZE = 64
-ABI_VERSION = 1
+DQ_GROUP = 256
+ABI_VERSION = 2
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libmoeq.so")
@@ -44,7 +46,7 @@ class _QW(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
                 ("blocksize", ctypes.c_int32), ("qdata", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("scale_codes", ctypes.c_void_p)]
 
 
 def library_path():
@@ -67,6 +69,7 @@ def _load():
         "moeq_nf4_codebook": (I32, [ctypes.POINTER(ctypes.c_float)]),
         "moeq_quantize_nf4": (I32, [P, QP, P]),
         "moeq_quantize_int8_rowwise": (I32, [P, QP, P]),
+        "moeq_compress_absmax": (I32, [QP, QP, P]),
         "moeq_dequantize": (I32, [QP, P, P]),
         "moeq_experts_forward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
         "moeq_experts_forward": (I32, [P, P, P, I32, I32, QP, QP, P, P, SZ, P]),
@@ -112,54 +115,67 @@ def _dev(t, dtype, name):
 
 
 class QWeight:
-    """A quantized expert tensor ``[E, rows, cols]``: packed codes plus fp32 scales.
+    """A quantized expert tensor ``[E, rows, cols]``: packed codes plus scales.
 
     NF4: ``qdata`` uint8 ``[E, rows, cols/2]``, ``scales`` fp32 absmax
     ``[E, rows*cols/64]``.  int8: ``qdata`` int8 ``[E, rows, cols]``,
-    ``scales`` fp32 ``[E, rows]``.  Plain tensors, so they serialise with
-    ``torch.save``.
+    ``scales`` fp32 ``[E, rows]``.  NF4 with double-quantized absmax: NF4
+    ``qdata``, ``scale_codes`` uint8 ``[E, rows*cols/64]`` and ``scales``
+    fp32 group scales ``[E, ceil(rows*cols/64 / 256)]``.  Plain tensors, so
+    they serialise with ``torch.save``.
     """
 
-    def __init__(self, fmt, num_experts, rows, cols, qdata, scales):
+    def __init__(self, fmt, num_experts, rows, cols, qdata, scales, scale_codes=None):
         self.format = fmt
         self.num_experts, self.rows, self.cols = int(num_experts), int(rows), int(cols)
-        self.blocksize = NF4_BLOCKSIZE if fmt == FMT_NF4 else self.cols
-        self.qdata, self.scales = qdata, scales
+        self.blocksize = NF4_BLOCKSIZE if fmt in (FMT_NF4, FMT_NF4_DQ) else self.cols
+        self.qdata, self.scales, self.scale_codes = qdata, scales, scale_codes
 
     @classmethod
     def empty(cls, fmt, num_experts, rows, cols, device):
         E, R, C = int(num_experts), int(rows), int(cols)
-        if fmt == FMT_NF4:
+        codes = None
+        if fmt in (FMT_NF4, FMT_NF4_DQ):
+            nb = R * (C // NF4_BLOCKSIZE)
             q = torch.empty((E, R, C // 2), dtype=torch.uint8, device=device)
-            s = torch.empty((E, R * (C // NF4_BLOCKSIZE)), dtype=torch.float32, device=device)
+            if fmt == FMT_NF4:
+                s = torch.empty((E, nb), dtype=torch.float32, device=device)
+            else:
+                s = torch.empty((E, (nb + DQ_GROUP - 1) // DQ_GROUP), dtype=torch.float32, device=device)
+                codes = torch.empty((E, nb), dtype=torch.uint8, device=device)
         elif fmt == FMT_INT8_ROWWISE:
             q = torch.empty((E, R, C), dtype=torch.int8, device=device)
             s = torch.empty((E, R), dtype=torch.float32, device=device)
         else:
             raise ValueError(f"unknown format {fmt}")
-        return cls(fmt, E, R, C, q, s)
+        return cls(fmt, E, R, C, q, s, codes)
 
     @property
     def shape(self):
         return (self.num_experts, self.rows, self.cols)
 
+    def _tensors(self):
+        return [t for t in (self.qdata, self.scales, self.scale_codes) if t is not None]
+
     def nbytes(self):
-        return self.qdata.numel() * self.qdata.element_size() + self.scales.numel() * 4
+        return sum(t.numel() * t.element_size() for t in self._tensors())
 
     def expert(self, e):
         """Expert ``e`` alone (E = 1), sharing storage."""
-        return QWeight(self.format, 1, self.rows, self.cols, self.qdata[e:e + 1], self.scales[e:e + 1])
+        codes = self.scale_codes[e:e + 1] if self.scale_codes is not None else None
+        return QWeight(self.format, 1, self.rows, self.cols, self.qdata[e:e + 1], self.scales[e:e + 1], codes)
 
     def like(self, device, pin_memory=False):
         """An empty QWeight of the same format and shape on ``device`` (host
         tensors pinned when ``pin_memory``)."""
-        q = torch.empty(self.qdata.shape, dtype=self.qdata.dtype, device=device, pin_memory=pin_memory)
-        s = torch.empty(self.scales.shape, dtype=self.scales.dtype, device=device, pin_memory=pin_memory)
-        return QWeight(self.format, self.num_experts, self.rows, self.cols, q, s)
+        new = [torch.empty(t.shape, dtype=t.dtype, device=device, pin_memory=pin_memory) for t in self._tensors()]
+        codes = new[2] if len(new) == 3 else None
+        return QWeight(self.format, self.num_experts, self.rows, self.cols, new[0], new[1], codes)
 
     def _c(self):
+        codes = self.scale_codes.data_ptr() if self.scale_codes is not None else None
         return _QW(self.format, self.num_experts, self.rows, self.cols, self.blocksize,
-                   self.qdata.data_ptr(), self.scales.data_ptr())
+                   self.qdata.data_ptr(), self.scales.data_ptr(), codes)
 
 
 def moeq_abi_version():
@@ -176,15 +192,34 @@ def moeq_nf4_codebook():
     return [float(v) for v in buf]
 
 
-def moeq_quantize_nf4(w, out=None, stream=None):
-    """bf16 ``[E, rows, cols]`` -> NF4 :class:`QWeight` (blocksize 64)."""
+def moeq_quantize_nf4(w, out=None, stream=None, double_quant=False):
+    """bf16 ``[E, rows, cols]`` -> NF4 :class:`QWeight` (blocksize 64), with
+    the absmax double-quantized when ``double_quant`` (or ``out`` has that
+    format)."""
     _dev(w, torch.bfloat16, "w")
     if w.dim() != 3:
         raise ValueError("w must be [E, rows, cols]")
-    q = out if out is not None else QWeight.empty(FMT_NF4, *w.shape, device=w.device)
+    fmt = FMT_NF4_DQ if double_quant else FMT_NF4
+    q = out if out is not None else QWeight.empty(fmt, *w.shape, device=w.device)
     qc = q._c()
     _check(_load().moeq_quantize_nf4(_ptr(w), ctypes.byref(qc), _stream(stream)), "moeq_quantize_nf4")
     return q
+
+
+def moeq_compress_absmax(src, out=None, share_codes=True, stream=None):
+    """NF4 :class:`QWeight` -> the same weights with double-quantized absmax.
+    With ``share_codes`` the result uses ``src.qdata`` itself; otherwise the
+    packed codes are copied into ``out`` (or a new buffer)."""
+    if src.format != FMT_NF4:
+        raise ValueError("moeq_compress_absmax takes an NF4 QWeight")
+    if out is None:
+        out = QWeight.empty(FMT_NF4_DQ, *src.shape, device=src.qdata.device)
+        if share_codes:
+            out.qdata = src.qdata
+    sc, oc = src._c(), out._c()
+    _check(_load().moeq_compress_absmax(ctypes.byref(sc), ctypes.byref(oc), _stream(stream)),
+           "moeq_compress_absmax")
+    return out
 
 
 def moeq_quantize_int8_rowwise(w, out=None, stream=None):
@@ -313,10 +348,10 @@ def moeq_router_topk(hidden, gate, K, renormalize=False, top_k_index=None, top_k
 def moeq_qweight_copy_async(src, dst, stream=None):
     """Asynchronous copy of a packed tensor between pinned host and device
     memory (either direction) on ``stream`` (default: torch's current)."""
-    if src.qdata.device.type == "cpu" and not src.qdata.is_pinned():
-        raise ValueError("host source must be pinned")
-    if dst.qdata.device.type == "cpu" and not dst.qdata.is_pinned():
-        raise ValueError("host destination must be pinned")
+    for name, q in (("source", src), ("destination", dst)):
+        for t in q._tensors():
+            if t.device.type == "cpu" and not t.is_pinned():
+                raise ValueError(f"host {name} must be pinned")
     s, d = src._c(), dst._c()
     _check(_load().moeq_qweight_copy_async(ctypes.byref(s), ctypes.byref(d), _stream(stream)),
            "moeq_qweight_copy_async")

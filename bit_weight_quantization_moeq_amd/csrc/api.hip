@@ -14,23 +14,46 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shape / format validation of one qweight descriptor.
+bool nf4_codes(int32_t format) { return format == MOEQ_FMT_NF4 || format == MOEQ_FMT_NF4_DQ; }
+
 moeq_status check_qweight(const moeq_qweight* q, int32_t want_format /* 0 = any */) {
   if (!q) return MOEQ_EINVAL;
-  if (q->format != MOEQ_FMT_NF4 && q->format != MOEQ_FMT_INT8_ROWWISE) return MOEQ_EFORMAT;
+  if (q->format != MOEQ_FMT_NF4 && q->format != MOEQ_FMT_INT8_ROWWISE && q->format != MOEQ_FMT_NF4_DQ)
+    return MOEQ_EFORMAT;
   if (want_format && q->format != want_format) return MOEQ_EFORMAT;
   if (q->num_experts <= 0 || q->rows <= 0 || q->cols <= 0) return MOEQ_EINVAL;
   if (!q->qdata || !q->scales) return MOEQ_EINVAL;
-  if (q->format == MOEQ_FMT_NF4) {
+  // absmax codes exactly when the format has them
+  if ((q->format == MOEQ_FMT_NF4_DQ) != (q->scale_codes != nullptr)) return MOEQ_EINVAL;
+  if (nf4_codes(q->format)) {
     if (q->blocksize != MOEQ_NF4_BLOCKSIZE || q->cols % MOEQ_NF4_BLOCKSIZE != 0) return MOEQ_EBLOCK;
   } else {
     if (q->blocksize != q->cols) return MOEQ_EBLOCK;
     if (q->cols % 8 != 0) return MOEQ_ESHAPE;
   }
   if (!aligned16(q->qdata) || !aligned16(q->scales)) return MOEQ_EALIGN;
+  if (q->scale_codes && !aligned16(q->scale_codes)) return MOEQ_EALIGN;
   return MOEQ_OK;
 }
 
 int64_t numel(const moeq_qweight* q) { return (int64_t)q->num_experts * q->rows * q->cols; }
+
+// NF4 blocks per expert
+int64_t blocks_per_expert(const moeq_qweight* q) { return (int64_t)q->rows * q->cols / kNf4Block; }
+
+// Bytes of codes, fp32 scales and absmax codes of one tensor.
+size_t code_bytes(const moeq_qweight* q) { return (size_t)(nf4_codes(q->format) ? numel(q) / 2 : numel(q)); }
+size_t scale_bytes(const moeq_qweight* q) {
+  const int64_t E = q->num_experts;
+  switch (q->format) {
+    case MOEQ_FMT_NF4: return sizeof(float) * (size_t)(E * blocks_per_expert(q));
+    case MOEQ_FMT_NF4_DQ: return sizeof(float) * (size_t)(E * dq_groups(blocks_per_expert(q)));
+    default: return sizeof(float) * (size_t)(E * q->rows);
+  }
+}
+size_t scale_code_bytes(const moeq_qweight* q) {
+  return q->format == MOEQ_FMT_NF4_DQ ? (size_t)(q->num_experts * blocks_per_expert(q)) : 0;
+}
 
 moeq_status device_status(hipError_t e) { return e == hipSuccess ? MOEQ_OK : MOEQ_EDEVICE; }
 
@@ -105,7 +128,7 @@ int32_t moeq_abi_version(void) { return MOEQ_ABI_VERSION; }
 const char* moeq_status_string(moeq_status s) {
   switch (s) {
     case MOEQ_OK: return "ok";
-    case MOEQ_EINVAL: return "invalid argument (null pointer, non-positive dimension, K < 1 or T < 0)";
+    case MOEQ_EINVAL: return "invalid argument (null pointer, non-positive dimension, K < 1, T < 0, or absmax codes given for a format without them)";
     case MOEQ_ESHAPE: return "inconsistent or unsupported shapes";
     case MOEQ_EBLOCK: return "blocksize rule violated (NF4: blocksize 64 and cols % 64 == 0; int8: blocksize == cols)";
     case MOEQ_EFORMAT: return "format tag not what the call needs, or gate_up and down formats differ";
@@ -123,13 +146,34 @@ moeq_status moeq_nf4_codebook(float* out) {
 }
 
 moeq_status moeq_quantize_nf4(const uint16_t* w, const moeq_qweight* dst, void* stream) {
-  moeq_status st = check_qweight(dst, MOEQ_FMT_NF4);
+  moeq_status st = check_qweight(dst, 0);
   if (st != MOEQ_OK) return st;
+  if (!nf4_codes(dst->format)) return MOEQ_EFORMAT;
   if (!w) return MOEQ_EINVAL;
   if (!aligned16(w)) return MOEQ_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dst->format == MOEQ_FMT_NF4_DQ)
+    return device_status(launch_quantize_nf4_dq(w, static_cast<uint8_t*>(dst->qdata), dst->scale_codes,
+                                                dst->scales, dst->num_experts, blocks_per_expert(dst), s));
   const int64_t nblocks = numel(dst) / kNf4Block;
-  return device_status(launch_quantize_nf4(w, static_cast<uint8_t*>(dst->qdata), dst->scales, nblocks,
-                                           static_cast<hipStream_t>(stream)));
+  return device_status(launch_quantize_nf4(w, static_cast<uint8_t*>(dst->qdata), dst->scales, nblocks, s));
+}
+
+moeq_status moeq_compress_absmax(const moeq_qweight* src, const moeq_qweight* dst, void* stream) {
+  moeq_status st = check_qweight(src, MOEQ_FMT_NF4);
+  if (st != MOEQ_OK) return st;
+  st = check_qweight(dst, MOEQ_FMT_NF4_DQ);
+  if (st != MOEQ_OK) return st;
+  if (src->num_experts != dst->num_experts || src->rows != dst->rows || src->cols != dst->cols)
+    return MOEQ_ESHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (dst->qdata != src->qdata)
+    e = hipMemcpyAsync(dst->qdata, src->qdata, code_bytes(src), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_compress_absmax(src->scales, dst->scale_codes, dst->scales, src->num_experts,
+                               blocks_per_expert(src), s);
+  return device_status(e);
 }
 
 moeq_status moeq_quantize_int8_rowwise(const uint16_t* w, const moeq_qweight* dst, void* stream) {
@@ -151,6 +195,9 @@ moeq_status moeq_dequantize(const moeq_qweight* src, uint16_t* out, void* stream
   if (src->format == MOEQ_FMT_NF4)
     return device_status(launch_dequantize_nf4(static_cast<const uint8_t*>(src->qdata), src->scales, out,
                                                numel(src) / kNf4Block, s));
+  if (src->format == MOEQ_FMT_NF4_DQ)
+    return device_status(launch_dequantize_nf4_dq(static_cast<const uint8_t*>(src->qdata), src->scale_codes,
+                                                  src->scales, out, src->num_experts, blocks_per_expert(src), s));
   return device_status(launch_dequantize_int8(static_cast<const int8_t*>(src->qdata), src->scales, out,
                                               (int64_t)src->num_experts * src->rows, src->cols, s));
 }
@@ -185,8 +232,8 @@ moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, co
   a.x = x; a.idx = idx; a.wts = wts;
   a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
   a.format = gu->format;
-  a.gu_q = gu->qdata; a.gu_s = gu->scales;
-  a.dn_q = dn->qdata; a.dn_s = dn->scales;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales; a.gu_c = gu->scale_codes;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
   a.out = out;
   a.rb = route_buffers(workspace, L);
   a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
@@ -245,8 +292,8 @@ moeq_status moeq_experts_backward(const uint16_t* x, const int32_t* idx, const f
   a.x = x; a.idx = idx; a.wts = wts; a.dout = dout;
   a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
   a.format = gu->format;
-  a.gu_q = gu->qdata; a.gu_s = gu->scales;
-  a.dn_q = dn->qdata; a.dn_s = dn->scales;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales; a.gu_c = gu->scale_codes;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
   a.grad_x = grad_x; a.grad_w = grad_w;
   a.rb = route_buffers(workspace, L.route);
   a.h = reinterpret_cast<uint16_t*>(w + L.h);
@@ -275,13 +322,11 @@ moeq_status moeq_qweight_copy_async(const moeq_qweight* src, const moeq_qweight*
   if (st != MOEQ_OK) return st;
   if (src->num_experts != dst->num_experts || src->rows != dst->rows || src->cols != dst->cols)
     return MOEQ_ESHAPE;
-  const int64_t n = numel(src);
-  const size_t code_bytes = (size_t)(src->format == MOEQ_FMT_NF4 ? n / 2 : n);
-  const size_t scale_bytes =
-      sizeof(float) * (size_t)(src->format == MOEQ_FMT_NF4 ? n / kNf4Block : (int64_t)src->num_experts * src->rows);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(dst->qdata, src->qdata, code_bytes, hipMemcpyDefault, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(dst->scales, src->scales, scale_bytes, hipMemcpyDefault, s);
+  hipError_t e = hipMemcpyAsync(dst->qdata, src->qdata, code_bytes(src), hipMemcpyDefault, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst->scales, src->scales, scale_bytes(src), hipMemcpyDefault, s);
+  if (e == hipSuccess && src->scale_codes)
+    e = hipMemcpyAsync(dst->scale_codes, src->scale_codes, scale_code_bytes(src), hipMemcpyDefault, s);
   return device_status(e);
 }
 

@@ -87,6 +87,70 @@ template <>
 struct Fmt<MOEQ_FMT_INT8_ROWWISE> {
   static constexpr int kStep = 64;
 };
+template <>
+struct Fmt<MOEQ_FMT_NF4_DQ> : Fmt<MOEQ_FMT_NF4> {};
+
+// NF4 codes (plain or with double-quantized absmax): 4-bit codes, 64-blocks.
+template <int FMT>
+constexpr bool kNf4Codes = FMT == MOEQ_FMT_NF4 || FMT == MOEQ_FMT_NF4_DQ;
+
+// One scale as loaded: NF4 / int8 hold the fp32 scale itself; with
+// double-quantized absmax, the absmax code and its group's scale, multiplied
+// only when the scale is used (after the loads have landed):
+// absmax' = fp32(code * group_scale).
+template <int FMT>
+struct Scale {
+  float s;
+  __device__ __forceinline__ float value() const { return s; }
+  __device__ __forceinline__ Scale masked(uint32_t m) const { return {__uint_as_float(__float_as_uint(s) & m)}; }
+  __device__ __forceinline__ Scale or_zero(bool in) const { return {in ? s : 0.0f}; }
+};
+template <>
+struct Scale<MOEQ_FMT_NF4_DQ> {
+  uint32_t c;
+  float g;
+  __device__ __forceinline__ float value() const { return (float)c * g; }
+  __device__ __forceinline__ Scale masked(uint32_t m) const { return {c, __uint_as_float(__float_as_uint(g) & m)}; }
+  __device__ __forceinline__ Scale or_zero(bool in) const { return {c, in ? g : 0.0f}; }
+};
+
+// Where one weight row's scales live.  load(boff): the scale of block boff
+// counted from the row's first block (int8: the row scale, boff rows on).
+template <int FMT>
+struct SRow {
+  const float* p;
+  static constexpr int kLoads = 1;
+  __device__ __forceinline__ Scale<FMT> load(int64_t boff) const { return {p[boff]}; }
+};
+// Double-quantized absmax: the row's absmax codes, its expert's group scales
+// and the row's first block within the expert (groups of 256 blocks of one
+// expert).
+template <>
+struct SRow<MOEQ_FMT_NF4_DQ> {
+  const uint8_t* c;
+  const float* g;
+  int64_t b0;
+  static constexpr int kLoads = 2;
+  __device__ __forceinline__ Scale<MOEQ_FMT_NF4_DQ> load(int64_t boff) const {
+    return {(uint32_t)c[boff], g[(b0 + boff) >> kDqGroupShift]};
+  }
+};
+
+// Scales of row `row` of expert e, from column block kb0 on, in a tensor of R
+// rows per expert and K columns.  ws: fp32 scales (NF4, int8) or group
+// scales (double-quantized); wc: absmax codes (double-quantized only).
+template <int FMT>
+__device__ __forceinline__ SRow<FMT> srow_at(const float* ws, const uint8_t* wc, int e, int R, int row, int K,
+                                             int kb0) {
+  if constexpr (FMT == MOEQ_FMT_NF4_DQ) {
+    const int64_t spr = K / kNf4Block, nb = (int64_t)R * spr;
+    return {wc + (int64_t)e * nb + row * spr + kb0, ws + (int64_t)e * dq_groups(nb), row * spr + kb0};
+  } else if constexpr (FMT == MOEQ_FMT_NF4) {
+    return {ws + ((int64_t)e * R + row) * (K / kNf4Block) + kb0};
+  } else {
+    return {ws + (int64_t)e * R + row};
+  }
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -180,27 +244,27 @@ __device__ __forceinline__ bf16x8 i8_frag(uint32_t w0, uint32_t w1, float s, flo
 template <int FMT>
 struct RowCodes {
   uint4 c0, c1;
-  float scale;
+  Scale<FMT> scale;
 
-  // Exactly three vector loads per call (the K-step pipeline counts on it):
-  // row_base: codes of the row (always a valid row); srow: scale pointer of
-  // the row (NF4: its first block); k0: K step start; hh: lane half; K: row
-  // length; ok: the row is real.  Outside the row or the K range the loads
-  // read the row start and the result is replaced by zeros.
-  static constexpr int kLoads = 3;
-  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K,
+  // Exactly kLoads vector loads per call (the K-step pipeline counts on it):
+  // row_base: codes of the row (always a valid row); srow: scales of the
+  // row; k0: K step start; hh: lane half; K: row length; ok: the row is
+  // real.  Outside the row or the K range the loads read the row start and
+  // the result is replaced by zeros.
+  static constexpr int kLoads = 2 + SRow<FMT>::kLoads;
+  __device__ __forceinline__ void fetch(const uint8_t* row_base, const SRow<FMT>& srow, int k0, int hh, int K,
                                         bool ok) {
     constexpr int half = Fmt<FMT>::kStep / 2;
     const int kk = k0 + half * hh;
     const bool in = ok && kk < K;
     const int kc = in ? kk : 0;
-    const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kc / 2 : kc));
+    const uint4* p = reinterpret_cast<const uint4*>(row_base + (kNf4Codes<FMT> ? kc / 2 : kc));
     const uint4 a = p[0], b = p[1];
-    const float sc = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : srow[0];
+    const Scale<FMT> sc = srow.load(kNf4Codes<FMT> ? kc / kNf4Block : 0);
     // NF4: zero absmax -> all-zero table; int8: zero scale -> the A operand is exactly zero
     c0 = in ? a : make_uint4(0, 0, 0, 0);
     c1 = in ? b : make_uint4(0, 0, 0, 0);
-    scale = in ? sc : 0.0f;
+    scale = sc.or_zero(in);
   }
   __device__ __forceinline__ uint32_t word(int i) const {
     const uint4& c = (i < 4) ? c0 : c1;
@@ -222,45 +286,43 @@ struct StreamCodes {
   // row_scale: the int8 row scale, loaded once by the caller (a per-step
   // load of a loop-invariant value would be hoisted to just before the loop
   // and make every step wait for it); unused for NF4.
-  __device__ __forceinline__ void fetch(const uint8_t* row_base, const float* srow, int k0, int hh, int K, bool ok,
-                                        float row_scale) {
+  __device__ __forceinline__ void fetch(const uint8_t* row_base, const SRow<FMT>& srow, int k0, int hh, int K,
+                                        bool ok, float row_scale) {
     constexpr int half = Fmt<FMT>::kStep / 2;
     const int kk = k0 + half * hh;
     const bool in = ok && kk < K;
     const int kc = in ? kk : 0;
-    const uint4* p = reinterpret_cast<const uint4*>(row_base + (FMT == MOEQ_FMT_NF4 ? kc / 2 : kc));
+    const uint4* p = reinterpret_cast<const uint4*>(row_base + (kNf4Codes<FMT> ? kc / 2 : kc));
     raw.c0 = p[0];
     raw.c1 = p[1];
-    raw.scale = (FMT == MOEQ_FMT_NF4) ? srow[kc / kNf4Block] : row_scale;
+    if constexpr (kNf4Codes<FMT>)
+      raw.scale = srow.load(kc / kNf4Block);
+    else
+      raw.scale = {row_scale};
     m = in ? 0xffffffffu : 0u;
     asm volatile("" : "+v"(m));  // opaque, so the select is not folded into a branch around the loads
   }
   __device__ __forceinline__ RowCodes<FMT> use() const {
     RowCodes<FMT> r = raw;
-    r.scale = __uint_as_float(__float_as_uint(raw.scale) & m);
+    r.scale = raw.scale.masked(m);
     return r;
   }
 };
 
 template <int FMT>
-struct Dequant;
-
-template <>
-struct Dequant<MOEQ_FMT_NF4> {
+struct Dequant {  // NF4, plain or with double-quantized absmax
   Nf4Table t;
-  __device__ __forceinline__ void prepare(const RowCodes<MOEQ_FMT_NF4>& r) { t = nf4_table(r.scale); }
+  __device__ __forceinline__ void prepare(const RowCodes<FMT>& r) { t = nf4_table(r.scale.value()); }
   // MFMA step s (0..7) of the K step: codes word s = 8 consecutive k of the block
-  __device__ __forceinline__ bf16x8 frag(const RowCodes<MOEQ_FMT_NF4>& r, int s) const {
-    return nf4_frag(t, r.word(s));
-  }
+  __device__ __forceinline__ bf16x8 frag(const RowCodes<FMT>& r, int s) const { return nf4_frag(t, r.word(s)); }
 };
 
 template <>
 struct Dequant<MOEQ_FMT_INT8_ROWWISE> {
   float s, ns128;
   __device__ __forceinline__ void prepare(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r) {
-    s = r.scale;
-    ns128 = -128.0f * r.scale;
+    s = r.scale.value();
+    ns128 = -128.0f * s;
   }
   // MFMA step s (0..3): 8 consecutive int8 codes = words 2s, 2s+1
   __device__ __forceinline__ bf16x8 frag(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r, int s_) const {
@@ -343,8 +405,8 @@ struct Core {
   // instruction i; K: reduction length; (q0, s0) / (q1, s1): this lane's two
   // weight rows.
   __device__ __forceinline__ static void run(char* sX, int buf_bytes, const char* tbase, const uint32_t (&roff)[kInstr],
-                                             int K, const uint8_t* q0, const float* s0, const uint8_t* q1,
-                                             const float* s1, bool wave_on, f32x16 (&acc0)[NB],
+                                             int K, const uint8_t* q0, const SRow<FMT>& s0, const uint8_t* q1,
+                                             const SRow<FMT>& s1, bool wave_on, f32x16 (&acc0)[NB],
                                              f32x16 (&acc1)[NB]) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -484,8 +546,8 @@ struct Lds {
 // ---------------------------------------------------------------------------
 template <int FMT, int NB>
 __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32_t* prow, int K, int H, int I,
-                                        int jcol, bool wave_on, const uint8_t* gq, const float* gs,
-                                        const uint8_t* uq, const float* us, int row0, int nrows,
+                                        int jcol, bool wave_on, const uint8_t* gq, const SRow<FMT>& gs,
+                                        const uint8_t* uq, const SRow<FMT>& us, int row0, int nrows,
                                         uint16_t* __restrict__ h, float* __restrict__ gu_save) {
   using C = Core<FMT, NB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -537,7 +599,7 @@ __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict__ x, int32_t K, int32_t E,
                                                      int32_t H, int32_t I, const uint8_t* __restrict__ wq,
-                                                     const float* __restrict__ ws,
+                                                     const float* __restrict__ ws, const uint8_t* __restrict__ wsc,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx,
@@ -553,15 +615,13 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
   const int jcol = ct * kG1Cols + 32 * wave;
   const bool wave_on = jcol < I;  // I % 32 == 0
   // (a wave past the last column streams the expert's first rows, unused)
-  const int64_t grow = (int64_t)e * 2 * I + (wave_on ? jcol : 0) + l32;
-  const int64_t urow = grow + I;
-  const int cpr = (FMT == MOEQ_FMT_NF4) ? H / 2 : H;  // code bytes per row
-  const int spr = (FMT == MOEQ_FMT_NF4) ? H / kNf4Block : 1;
+  const int grow = (wave_on ? jcol : 0) + l32, urow = grow + I;  // rows within the expert
+  const int cpr = kNf4Codes<FMT> ? H / 2 : H;                     // code bytes per row
 
-  const uint8_t* gq = wq + grow * cpr;
-  const uint8_t* uq = wq + urow * cpr;
-  const float* gs = ws + grow * spr;
-  const float* us = ws + urow * spr;
+  const uint8_t* gq = wq + ((int64_t)e * 2 * I + grow) * cpr;
+  const uint8_t* uq = wq + ((int64_t)e * 2 * I + urow) * cpr;
+  const SRow<FMT> gs = srow_at<FMT>(ws, wsc, e, 2 * I, grow, H, 0);
+  const SRow<FMT> us = srow_at<FMT>(ws, wsc, e, 2 * I, urow, H, 0);
   const int32_t* prow = perm_idx + row0;
   if (nrows > 192)
     g1_tile<FMT, 8>(sX, x, prow, K, H, I, jcol, wave_on, gq, gs, uq, us, row0, nrows, h, gu_save);
@@ -579,8 +639,8 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 template <int FMT, int NB>
 __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_t* h, int H, int I, int ncol,
-                                        bool on, const uint8_t* q0, const float* s0, const uint8_t* q1,
-                                        const float* s1, int row0, int nrows, float* __restrict__ y) {
+                                        bool on, const uint8_t* q0, const SRow<FMT>& s0, const uint8_t* q1,
+                                        const SRow<FMT>& s1, int row0, int nrows, float* __restrict__ y) {
   using C = Core<FMT, NB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t roff[C::kInstr];  // byte offset of each staged h row (relative to the tile's first row)
@@ -619,6 +679,7 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict__ h, const float* __restrict__ wts,
                                                      int32_t E, int32_t H, int32_t I,
                                                      const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                                                     const uint8_t* __restrict__ wsc,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx, float* __restrict__ y) {
@@ -635,14 +696,13 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 
   const int ncol = ct * kG2Rows + 64 * wave;  // H % 64 == 0: a wave is all in or all out
   const bool on = ncol < H;
-  const int64_t r0 = (int64_t)e * H + (on ? ncol : 0) + l32, r1 = r0 + 32;
-  const int cpr = (FMT == MOEQ_FMT_NF4) ? I / 2 : I;
-  const int spr = (FMT == MOEQ_FMT_NF4) ? I / kNf4Block : 1;
+  const int r0 = (on ? ncol : 0) + l32, r1 = r0 + 32;  // rows within the expert
+  const int cpr = kNf4Codes<FMT> ? I / 2 : I;
 
-  const uint8_t* q0 = wq + r0 * cpr;
-  const uint8_t* q1 = wq + r1 * cpr;
-  const float* s0 = ws + r0 * spr;
-  const float* s1 = ws + r1 * spr;
+  const uint8_t* q0 = wq + ((int64_t)e * H + r0) * cpr;
+  const uint8_t* q1 = wq + ((int64_t)e * H + r1) * cpr;
+  const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, H, r0, I, 0);
+  const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, H, r1, I, 0);
   if (nrows > 192)
     g2_tile<FMT, 8>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else if (nrows > 128)
@@ -687,6 +747,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
                                                         int32_t E, int32_t H, int32_t I, int32_t P,
                                                         const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ ws,
+                                                        const uint8_t* __restrict__ wsc,
                                                         uint16_t* __restrict__ hout, float* __restrict__ yout) {
   constexpr int kT = NW * 64;
   constexpr int kJ = kDecodeMax / kT;  // assignments per thread
@@ -746,19 +807,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   const int rbi = blockIdx.y * RB + wave / P, part = wave % P;
   const bool on = rbi < nrb;  // a wave past the last row block streams block 0 and stores nothing
   const int col0 = (on ? rbi : 0) * (G1 ? 32 : 64);
-  const int64_t r0 = G1 ? (int64_t)e * 2 * I + col0 + l32 : (int64_t)e * H + col0 + l32;
-  const int64_t r1 = G1 ? r0 + I : r0 + 32;
-  const int cpr = (FMT == MOEQ_FMT_NF4) ? K / 2 : K;
-  const int spr = (FMT == MOEQ_FMT_NF4) ? K / kNf4Block : 1;
-  const uint8_t* q0 = wq + r0 * cpr;
-  const uint8_t* q1 = wq + r1 * cpr;
-  const float* s0 = ws + r0 * spr;
-  const float* s1 = ws + r1 * spr;
+  const int R = G1 ? 2 * I : H;  // rows per expert
+  const int r0 = col0 + l32, r1 = G1 ? r0 + I : r0 + 32;  // rows within the expert
+  const int cpr = kNf4Codes<FMT> ? K / 2 : K;
+  const uint8_t* q0 = wq + ((int64_t)e * R + r0) * cpr;
+  const uint8_t* q1 = wq + ((int64_t)e * R + r1) * cpr;
+  const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, R, r0, K, 0);
+  const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, R, r1, K, 0);
   const int nks = (K + kStep - 1) / kStep, nkp = (nks + 1) / 2;  // steps, pairs of steps
   const int ks0 = 2 * (part * nkp / P), ks1 = min(2 * ((part + 1) * nkp / P), nks);
   // int8: the row scales, first of this wave's loads
-  const float rs0 = (FMT == MOEQ_FMT_NF4) ? 0.0f : s0[0];
-  const float rs1 = (FMT == MOEQ_FMT_NF4) ? 0.0f : s1[0];
+  float rs0 = 0.0f, rs1 = 0.0f;
+  if constexpr (!kNf4Codes<FMT>) {
+    rs0 = s0.p[0];
+    rs1 = s1.p[0];
+  }
   StreamCodes<FMT> ca0, ca1, cb0, cb1;
   ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1, rs0);
   ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1, rs1);
@@ -992,6 +1055,7 @@ template <int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restrict__ vsrc, int32_t Ktop, int32_t E,
                                                         int32_t R, int32_t C, const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ ws,
+                                                        const uint8_t* __restrict__ wsc,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ tile_start,
                                                         const int32_t* __restrict__ perm_idx,
@@ -1019,15 +1083,17 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
   const int wc = c0 + 32 * (t & 3);
   const bool wc_in = wc < C;  // C % 64 == 0: a 32-column quarter is wholly in or out
   const int wcc = wc_in ? wc : 0;
-  const int64_t cpr = (FMT == MOEQ_FMT_NF4) ? C / 2 : C;
-  const int64_t spr = (FMT == MOEQ_FMT_NF4) ? C / kNf4Block : 1;
-  const uint8_t* wrow = wq + ((int64_t)e * R + wr) * cpr + (FMT == MOEQ_FMT_NF4 ? wcc / 2 : wcc);
-  const float* srow = ws + ((int64_t)e * R + wr) * spr + (FMT == MOEQ_FMT_NF4 ? wcc / kNf4Block : 0);
+  const int64_t cpr = kNf4Codes<FMT> ? C / 2 : C;
+  const int64_t spr = kNf4Codes<FMT> ? C / kNf4Block : 1;
+  const uint8_t* wrow = wq + ((int64_t)e * R + wr) * cpr + (kNf4Codes<FMT> ? wcc / 2 : wcc);
+  const SRow<FMT> srow = srow_at<FMT>(ws, wsc, e, R, wr, C, kNf4Codes<FMT> ? wcc / kNf4Block : 0);
   struct WCodes {
     uint4 a, b;  // NF4: a (32 codes); int8: a, b
-    float s;
+    Scale<FMT> s;
     uint32_t m;  // all ones, or zero for a step or column quarter past the end
   };
+  // code loads plus scale loads per step
+  constexpr int kWLoads = (kNf4Codes<FMT> ? 1 : 2) + SRow<FMT>::kLoads;
   // Loads for step ks (past the last step: step 0's addresses).  They are
   // never behind a branch; a step or columns past the end are zeroed through
   // the scale when the codes are used (a zero scale makes the weights
@@ -1037,16 +1103,16 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     const int64_t kr = in ? (int64_t)ks * kTk : 0;
     const uint4* p = reinterpret_cast<const uint4*>(wrow + kr * cpr);
     c.a = p[0];
-    if (FMT != MOEQ_FMT_NF4) c.b = p[1];
-    c.s = srow[kr * spr];
+    if constexpr (!kNf4Codes<FMT>) c.b = p[1];
+    c.s = srow.load(kr * spr);
     uint32_t m = (in && wc_in) ? 0xffffffffu : 0u;
     asm volatile("" : "+v"(m));  // opaque: keeps the select from becoming a branch around the loads
     c.m = m;
   };
   auto wstore = [&](const WCodes& c, int buf) {
     char* dst = sW(buf) + wr * kTpitch + 64 * (t & 3);
-    const float sc = __uint_as_float(__float_as_uint(c.s) & c.m);
-    if constexpr (FMT == MOEQ_FMT_NF4) {
+    const float sc = c.s.masked(c.m).value();
+    if constexpr (kNf4Codes<FMT>) {
       const Nf4Table tb = nf4_table(sc);
       *reinterpret_cast<bf16x8*>(dst) = nf4_frag(tb, c.a.x);
       *reinterpret_cast<bf16x8*>(dst + 16) = nf4_frag(tb, c.a.y);
@@ -1156,7 +1222,7 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     // DMA for step ks + 1) has landed, and this wave's LDS writes are done.
     // A release fence would also wait for the codes (LDS DMA counts as a
     // vector load), so the barrier is bare, with an acquire fence after it.
-    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<(FMT == MOEQ_FMT_NF4) ? 2 : 3>);
+    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWLoads>);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
@@ -1253,63 +1319,58 @@ DecodeShape decode_shape(int ux, int nrb) {
 
 template <int FMT, bool G1>
 void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const uint8_t* q, const float* sc,
-                        hipStream_t s) {
+                        const uint8_t* scc, hipStream_t s) {
   const int32_t n = a.T * a.K;
   const DecodeShape d = decode_shape(ux, G1 ? a.I / 32 : a.H / 64);
   decode_kernel<FMT, G1, kWaves><<<dim3(ux, d.gy), kThreads, 0, s>>>(act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p,
-                                                                     q, sc, a.h, a.y);
+                                                                     q, sc, scc, a.h, a.y);
 }
 
 template <int FMT>
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
   const int ux = a.E < n ? a.E : n;  // at most this many experts are touched
-  if (ev) hipEventRecord(ev[1], s);  // no routing stage on this path
-  launch_decode_gemm<FMT, true>(a, ux, a.x, static_cast<const uint8_t*>(a.gu_q), a.gu_s, s);
-  if (ev) hipEventRecord(ev[2], s);
-  launch_decode_gemm<FMT, false>(a, ux, a.h, static_cast<const uint8_t*>(a.dn_q), a.dn_s, s);
-  if (ev) hipEventRecord(ev[3], s);
+  if (ev) (void)hipEventRecord(ev[1], s);  // no routing stage on this path
+  launch_decode_gemm<FMT, true>(a, ux, a.x, static_cast<const uint8_t*>(a.gu_q), a.gu_s, a.gu_c, s);
+  if (ev) (void)hipEventRecord(ev[2], s);
+  launch_decode_gemm<FMT, false>(a, ux, a.h, static_cast<const uint8_t*>(a.dn_q), a.dn_s, a.dn_c, s);
+  if (ev) (void)hipEventRecord(ev[3], s);
   decode_combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.idx, a.K, a.E, a.H, a.out);
-  if (ev) hipEventRecord(ev[4], s);
+  if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();
 }
 
-hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
+template <int FMT>
+hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
-  if (ev) hipEventRecord(ev[0], s);
-  if (n <= kDecodeMax) {
-    return a.format == MOEQ_FMT_NF4 ? launch_decode<MOEQ_FMT_NF4>(a, s, ev)
-                                    : launch_decode<MOEQ_FMT_INT8_ROWWISE>(a, s, ev);
-  }
   hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
-  if (ev) hipEventRecord(ev[1], s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   // upper bound on the number of token tiles: sum_e ceil(count_e / kBM)
   const int mtiles = (n + kBM - 1) / kBM + a.E;
   const int g1 = round_up(mtiles * ((a.I + kG1Cols - 1) / kG1Cols), kXcds);
   const int g2 = round_up(mtiles * ((a.H + kG2Rows - 1) / kG2Rows), kXcds);
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
-  if (a.format == MOEQ_FMT_NF4) {
-    g1_kernel<MOEQ_FMT_NF4><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.rb.offsets,
-                                                    a.rb.tile_start, a.rb.perm, a.h, nullptr);
-    if (ev) hipEventRecord(ev[2], s);
-    g2_kernel<MOEQ_FMT_NF4><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.rb.offsets,
-                                                    a.rb.tile_start, a.rb.perm, a.y);
-  } else {
-    g1_kernel<MOEQ_FMT_INT8_ROWWISE><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s,
-                                                             a.rb.offsets, a.rb.tile_start, a.rb.perm, a.h, nullptr);
-    if (ev) hipEventRecord(ev[2], s);
-    g2_kernel<MOEQ_FMT_INT8_ROWWISE><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s,
-                                                             a.rb.offsets, a.rb.tile_start, a.rb.perm, a.y);
-  }
-  if (ev) hipEventRecord(ev[3], s);
+  g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, a.rb.offsets,
+                                         a.rb.tile_start, a.rb.perm, a.h, nullptr);
+  if (ev) (void)hipEventRecord(ev[2], s);
+  g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
+                                         a.rb.tile_start, a.rb.perm, a.y);
+  if (ev) (void)hipEventRecord(ev[3], s);
   combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.rb.slot, a.K, a.H, a.out);
-  if (ev) hipEventRecord(ev[4], s);
+  if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();
 }
 
-hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s) {
+template <int FMT>
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
+  if (ev) (void)hipEventRecord(ev[0], s);
+  return a.T * a.K <= kDecodeMax ? launch_decode<FMT>(a, s, ev) : launch_tiled<FMT>(a, s, ev);
+}
+
+template <int FMT>
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   const int32_t n = a.T * a.K;
   hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
@@ -1321,31 +1382,33 @@ hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s) {
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   const RouteBuffers& r = a.rb;
-  if (a.format == MOEQ_FMT_NF4) {
-    g1_kernel<MOEQ_FMT_NF4><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, r.offsets, r.tile_start,
-                                                    r.perm, a.h, a.gu_save);
-    g2_kernel<MOEQ_FMT_NF4><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
-                                                    r.tile_start, r.perm, a.zdx);
-    gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
-    tgemm_kernel<MOEQ_FMT_NF4, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
-                                                          r.tile_start, r.perm, a.wts, a.gu_save, a.dgu);
-    tgemm_kernel<MOEQ_FMT_NF4, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s, r.offsets,
-                                                          r.tile_start, r.perm, nullptr, nullptr, a.zdx);
-  } else {
-    g1_kernel<MOEQ_FMT_INT8_ROWWISE><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, r.offsets,
-                                                             r.tile_start, r.perm, a.h, a.gu_save);
-    g2_kernel<MOEQ_FMT_INT8_ROWWISE><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, r.offsets,
-                                                             r.tile_start, r.perm, a.zdx);
-    gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
-    tgemm_kernel<MOEQ_FMT_INT8_ROWWISE, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s,
-                                                                   r.offsets, r.tile_start, r.perm, a.wts,
-                                                                   a.gu_save, a.dgu);
-    tgemm_kernel<MOEQ_FMT_INT8_ROWWISE, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s,
-                                                                   r.offsets, r.tile_start, r.perm, nullptr,
-                                                                   nullptr, a.zdx);
-  }
+  g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, r.offsets, r.tile_start,
+                                         r.perm, a.h, a.gu_save);
+  g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets, r.tile_start,
+                                         r.perm, a.zdx);
+  gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
+  tgemm_kernel<FMT, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
+                                               r.tile_start, r.perm, a.wts, a.gu_save, a.dgu);
+  tgemm_kernel<FMT, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s, a.gu_c, r.offsets,
+                                               r.tile_start, r.perm, nullptr, nullptr, a.zdx);
   combine_kernel<<<a.T, kThreads, 0, s>>>(a.zdx, r.slot, a.K, a.H, a.grad_x);
   return hipGetLastError();
+}
+
+hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
+  switch (a.format) {
+    case MOEQ_FMT_NF4: return launch_forward<MOEQ_FMT_NF4>(a, s, ev);
+    case MOEQ_FMT_NF4_DQ: return launch_forward<MOEQ_FMT_NF4_DQ>(a, s, ev);
+    default: return launch_forward<MOEQ_FMT_INT8_ROWWISE>(a, s, ev);
+  }
+}
+
+hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s) {
+  switch (a.format) {
+    case MOEQ_FMT_NF4: return launch_backward<MOEQ_FMT_NF4>(a, s);
+    case MOEQ_FMT_NF4_DQ: return launch_backward<MOEQ_FMT_NF4_DQ>(a, s);
+    default: return launch_backward<MOEQ_FMT_INT8_ROWWISE>(a, s);
+  }
 }
 
 }  // namespace moeq

@@ -36,6 +36,14 @@ constexpr uint32_t kNf4ThresholdBits[15] = {
 constexpr int kNf4Block = 64;
 constexpr int kNf4ZeroCode = 7;
 
+// Double-quantized absmax: groups of 2^kDqGroupShift consecutive blocks of
+// one expert share one fp32 group scale.
+constexpr int kDqGroupShift = 8;
+static_assert((1 << kDqGroupShift) == MOEQ_DQ_GROUP, "group size");
+__host__ __device__ constexpr int64_t dq_groups(int64_t blocks_per_expert) {
+  return (blocks_per_expert + MOEQ_DQ_GROUP - 1) >> kDqGroupShift;
+}
+
 // The NF4 decision in the kernels first picks a bucket of width 1/16 in n
 // from an approximate ratio, then makes one exact threshold test.  Bucket j
 // covers n in [(j-17)/16, (j-16)/16); every bucket holds at most one
@@ -56,6 +64,13 @@ hipError_t launch_dequantize_nf4(const uint8_t* q, const float* absmax, uint16_t
                                  int64_t nblocks, hipStream_t s);
 hipError_t launch_dequantize_int8(const int8_t* q, const float* scale, uint16_t* out,
                                   int64_t nrows, int32_t cols, hipStream_t s);
+// Double-quantized absmax: nb blocks per expert, E experts.
+hipError_t launch_quantize_nf4_dq(const uint16_t* w, uint8_t* q, uint8_t* codes, float* gscale, int32_t E,
+                                  int64_t nb, hipStream_t s);
+hipError_t launch_compress_absmax(const float* absmax, uint8_t* codes, float* gscale, int32_t E, int64_t nb,
+                                  hipStream_t s);
+hipError_t launch_dequantize_nf4_dq(const uint8_t* q, const uint8_t* codes, const float* gscale, uint16_t* out,
+                                    int32_t E, int64_t nb, hipStream_t s);
 
 // Routing workspace carve-up (all int32).
 struct RouteBuffers {
@@ -80,9 +95,11 @@ struct ForwardArgs {
   int32_t T, K, E, H, I;
   int32_t format;
   const void* gu_q;         // gate_up codes
-  const float* gu_s;        // gate_up scales
+  const float* gu_s;        // gate_up scales (double-quantized: group scales)
+  const uint8_t* gu_c;      // gate_up absmax codes (double-quantized only)
   const void* dn_q;         // down codes
   const float* dn_s;        // down scales
+  const uint8_t* dn_c;
   uint16_t* out;            // [T][H]
   RouteBuffers rb;
   uint16_t* h;              // [T*K][I] bf16, expert-sorted rows
@@ -100,8 +117,10 @@ struct BackwardArgs {
   int32_t format;
   const void* gu_q;
   const float* gu_s;
+  const uint8_t* gu_c;
   const void* dn_q;
   const float* dn_s;
+  const uint8_t* dn_c;
   uint16_t* grad_x;         // [T][H]
   float* grad_w;            // [T][K]
   RouteBuffers rb;

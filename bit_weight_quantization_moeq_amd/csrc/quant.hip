@@ -6,10 +6,16 @@
 // int8: row-wise absmax, scale absmax/127 ("MoE Expert Quantization",
 // Implementation details).
 //
-// All four kernels are HBM-streaming: a 64-block or a row is read once with
+// NF4 with double-quantized absmax: the block absmax is itself stored as an
+// 8-bit code per block plus one fp32 scale per group of 256 blocks of one
+// expert (bitsandbytes issue #1849, Reproduction and maintainer thread:
+// double quantization of the statistics; the format is the library's own).
+//
+// All kernels are HBM-streaming: a 64-block or a row is read once with
 // 16-byte loads, reduced across lanes with DPP, and written once.  Since a
 // 64-block never straddles a row or an expert, an NF4 tensor is a flat array
-// of independent blocks and the kernels ignore E/rows/cols entirely.
+// of independent blocks and the plain kernels ignore E/rows/cols entirely;
+// the double-quantized ones work per group (one workgroup each).
 #include "moeq_internal.h"
 
 namespace moeq {
@@ -90,6 +96,40 @@ __device__ __forceinline__ uint32_t nf4_code(float w, float a, float r16, const 
   return e.y + ((__builtin_fmaf(a, __uint_as_float(e.x), -w) <= 0.0f) ? 1u : 0u);
 }
 
+// One 64-block per 8 lanes: v holds this lane's 8 consecutive bf16 of the
+// block.  Returns the lane's 8 codes as one word (column 2m in the high
+// nibble of byte m) and sets a to the block absmax (the same in all 8 lanes).
+// Every lane of the wave must call it (the sub-2^-90 rescue votes).
+__device__ __forceinline__ uint32_t nf4_block_word(uint4 v, const uint2* tab, float& a_out) {
+  float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  m = fmaxf(m, fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
+  const float a = group8_max(m);
+
+  // Blocks whose absmax is below 2^-90 (rare: denormal-range weights) are
+  // scaled by 2^100 first, which is exact and leaves every ratio unchanged.
+  float ae = a;
+  if (__any(a > 0.0f && a < 0x1p-90f)) {
+    const float sc = (a > 0.0f && a < 0x1p-90f) ? 0x1p100f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] *= sc;
+    ae = a * sc;
+  }
+  ae = (a == 0.0f) ? 1.0f : ae;  // all-zero block: every w is +-0 -> code 7
+  const float r16 = 16.0f * __builtin_amdgcn_rcpf(ae);
+
+  uint32_t word = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    const uint32_t hi = nf4_code(x[k], ae, r16, tab);
+    const uint32_t lo = nf4_code(x[k + 1], ae, r16, tab);
+    word |= ((hi << 4) | lo) << (4 * k);
+  }
+  a_out = a;
+  return word;
+}
+
 __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint4* __restrict__ w,
                                                                uint32_t* __restrict__ q,
                                                                float* __restrict__ absmax,
@@ -116,37 +156,85 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint4* __r
 #pragma unroll
     for (int u = 0; u < kNf4Unroll; ++u) {
       const int64_t b = base + u * 8 + grp;
-      float x[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
-                    bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
-      float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
-      const float a = group8_max(m);
-
-      // Blocks whose absmax is below 2^-90 (rare: denormal-range weights) are
-      // scaled by 2^100 first, which is exact and leaves every ratio unchanged.
-      float ae = a;
-      if (__any(a > 0.0f && a < 0x1p-90f)) {
-        const float sc = (a > 0.0f && a < 0x1p-90f) ? 0x1p100f : 1.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] *= sc;
-        ae = a * sc;
-      }
-      ae = (a == 0.0f) ? 1.0f : ae;  // all-zero block: every w is +-0 -> code 7
-      const float r16 = 16.0f * __builtin_amdgcn_rcpf(ae);
-
-      uint32_t word = 0;
-#pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const uint32_t hi = nf4_code(x[k], ae, r16, tab);
-        const uint32_t lo = nf4_code(x[k + 1], ae, r16, tab);
-        word |= ((hi << 4) | lo) << (4 * k);
-      }
+      float a;
+      const uint32_t word = nf4_block_word(v[u], tab, a);
       if (b < nblocks) {
         q[b * 8 + sub] = word;
         if (sub == 0) absmax[b] = a;
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Double-quantized absmax: one workgroup per group of (at most) 256
+// consecutive blocks of one expert.  Thread t owns block t of the group: the
+// group maximum m comes from a wave reduction and 4 LDS partials, then
+// s2 = fp32(m / 255) and c = rint(fp32(fp32(255 a) / m)) (IEEE division,
+// round half to even), exactly the row-wise int8 rule with 255 levels.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dq_group_encode(float a, int cnt, uint8_t* codes, float* gscale) {
+  __shared__ float part[kThreads / 64];
+  const int t = threadIdx.x;
+  const float m0 = wave_max(t < cnt ? a : 0.0f);
+  if ((t & 63) == 0) part[t >> 6] = m0;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  if (t < cnt) codes[t] = (m > 0.0f) ? (uint8_t)__builtin_rintf((a * 255.0f) / m) : (uint8_t)0;
+  if (t == 0) *gscale = m / 255.0f;
+}
+
+// NF4 quantize writing double-quantized absmax: wave w of the group's
+// workgroup quantizes blocks 64w .. 64w + 63 (8 per step, 4 steps of loads
+// in flight), keeping each absmax in LDS for the group encode.
+__global__ __launch_bounds__(kThreads) void nf4dq_quantize_kernel(const uint4* __restrict__ w,
+                                                                 uint32_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 float* __restrict__ gscale, int64_t nb,
+                                                                 int32_t ng) {
+  __shared__ uint2 tab[kNf4Buckets];
+  __shared__ float sa[MOEQ_DQ_GROUP];
+  if (threadIdx.x < kNf4Buckets) tab[threadIdx.x] = nf4_bucket_entry(threadIdx.x);
+  __syncthreads();
+  const int e = blockIdx.x / ng, g = blockIdx.x - e * ng;
+  const int64_t first = (int64_t)e * nb + (int64_t)g * MOEQ_DQ_GROUP;  // first block of the group
+  const int cnt = (int)min<int64_t>(MOEQ_DQ_GROUP, nb - (int64_t)g * MOEQ_DQ_GROUP);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 7, grp = lane >> 3;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint4 v[kNf4Unroll];
+#pragma unroll
+    for (int u = 0; u < kNf4Unroll; ++u) {
+      int j = 64 * wave + 32 * half + 8 * u + grp;  // block within the group
+      j = j < cnt ? j : cnt - 1;                    // clamp: every lane loads, only valid ones store
+      v[u] = ld_stream16(&w[(first + j) * 8 + sub]);
+    }
+#pragma unroll
+    for (int u = 0; u < kNf4Unroll; ++u) {
+      const int j = 64 * wave + 32 * half + 8 * u + grp;
+      float a;
+      const uint32_t word = nf4_block_word(v[u], tab, a);
+      if (j < cnt) {
+        q[(first + j) * 8 + sub] = word;
+        if (sub == 0) sa[j] = a;
+      }
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  dq_group_encode(t < cnt ? sa[t] : 0.0f, cnt, codes + first, gscale + (int64_t)e * ng + g);
+}
+
+// Double-quantize existing fp32 absmax [E][nb].
+__global__ __launch_bounds__(kThreads) void dq_compress_kernel(const float* __restrict__ absmax,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ gscale, int64_t nb, int32_t ng) {
+  const int e = blockIdx.x / ng, g = blockIdx.x - e * ng;
+  const int64_t first = (int64_t)e * nb + (int64_t)g * MOEQ_DQ_GROUP;
+  const int cnt = (int)min<int64_t>(MOEQ_DQ_GROUP, nb - (int64_t)g * MOEQ_DQ_GROUP);
+  const int t = threadIdx.x;
+  dq_group_encode(t < cnt ? absmax[first + t] : 0.0f, cnt, codes + first, gscale + (int64_t)e * ng + g);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,6 +323,36 @@ __global__ __launch_bounds__(kThreads) void nf4_dequantize_kernel(const uint32_t
   }
 }
 
+// NF4 with double-quantized absmax: one workgroup per group; the group
+// scale is read once and absmax' = fp32(c * s2) per block.
+__global__ __launch_bounds__(kThreads) void nf4dq_dequantize_kernel(const uint32_t* __restrict__ q,
+                                                                   const uint8_t* __restrict__ codes,
+                                                                   const float* __restrict__ gscale,
+                                                                   uint4* __restrict__ out, int64_t nb,
+                                                                   int32_t ng) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = __uint_as_float(kNf4LevelBits[threadIdx.x]);
+  __syncthreads();
+  const int e = blockIdx.x / ng, g = blockIdx.x - e * ng;
+  const int64_t first = (int64_t)e * nb + (int64_t)g * MOEQ_DQ_GROUP;
+  const int cnt = (int)min<int64_t>(MOEQ_DQ_GROUP, nb - (int64_t)g * MOEQ_DQ_GROUP);
+  const float s2 = gscale[(int64_t)e * ng + g];
+  for (int i = threadIdx.x; i < 8 * cnt; i += kThreads) {  // 8 words of codes per block
+    const int64_t d = first * 8 + i;
+    const uint32_t c = __builtin_nontemporal_load(&q[d]);
+    const float a = (float)codes[first + (i >> 3)] * s2;
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t byte = (c >> (8 * m)) & 0xffu;
+      v[2 * m] = lv[byte >> 4] * a;
+      v[2 * m + 1] = lv[byte & 0xfu] * a;
+    }
+    out[d] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                        pack_bf16x2(v[6], v[7]));
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void int8_dequantize_kernel(const uint2* __restrict__ q,
                                                                   const float* __restrict__ scale,
                                                                   uint4* __restrict__ out,
@@ -293,6 +411,29 @@ hipError_t launch_dequantize_int8(const int8_t* q, const float* scale, uint16_t*
   const int grid = grid_for(nchunks, kThreads, 16384);
   int8_dequantize_kernel<<<grid, kThreads, 0, s>>>(reinterpret_cast<const uint2*>(q), scale,
                                                     reinterpret_cast<uint4*>(out), nchunks, cpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nf4_dq(const uint16_t* w, uint8_t* q, uint8_t* codes, float* gscale, int32_t E,
+                                  int64_t nb, hipStream_t s) {
+  const int32_t ng = (int32_t)dq_groups(nb);
+  nf4dq_quantize_kernel<<<(unsigned)E * ng, kThreads, 0, s>>>(reinterpret_cast<const uint4*>(w),
+                                                               reinterpret_cast<uint32_t*>(q), codes, gscale, nb, ng);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_absmax(const float* absmax, uint8_t* codes, float* gscale, int32_t E, int64_t nb,
+                                  hipStream_t s) {
+  const int32_t ng = (int32_t)dq_groups(nb);
+  dq_compress_kernel<<<(unsigned)E * ng, kThreads, 0, s>>>(absmax, codes, gscale, nb, ng);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_nf4_dq(const uint8_t* q, const uint8_t* codes, const float* gscale, uint16_t* out,
+                                    int32_t E, int64_t nb, hipStream_t s) {
+  const int32_t ng = (int32_t)dq_groups(nb);
+  nf4dq_dequantize_kernel<<<(unsigned)E * ng, kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(q), codes, gscale,
+                                                                 reinterpret_cast<uint4*>(out), nb, ng);
   return hipGetLastError();
 }
 

@@ -74,5 +74,5 @@ class ExpertOffload:
 
 
 def _copy_host(src, dst):
-    dst.qdata.copy_(src.qdata)
-    dst.scales.copy_(src.scales)
+    for d, t in zip(dst._tensors(), src._tensors()):
+        d.copy_(t)

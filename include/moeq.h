@@ -31,14 +31,16 @@
 extern "C" {
 #endif
 
-#define MOEQ_ABI_VERSION 1
+#define MOEQ_ABI_VERSION 2
 #define MOEQ_NF4_BLOCKSIZE 64
+#define MOEQ_DQ_GROUP 256 /* NF4 blocks per double-quantization group */
 #define MOEQ_MAX_EXPERTS 1024
 
 typedef int32_t moeq_status;
 enum {
   MOEQ_OK = 0,
-  MOEQ_EINVAL = -1,     /* null pointer, a dimension <= 0, K < 1, T < 0            */
+  MOEQ_EINVAL = -1,     /* null pointer, a dimension <= 0, K < 1, T < 0, scale_codes
+                           set for a format without them (or missing for NF4_DQ)   */
   MOEQ_ESHAPE = -2,     /* gate_up / down / hidden dimensions inconsistent          */
   MOEQ_EBLOCK = -3,     /* NF4: blocksize != 64 or cols % 64 != 0; int8: blocksize != cols */
   MOEQ_EFORMAT = -4,    /* format tag not what the call needs, or gate_up and down differ */
@@ -47,7 +49,7 @@ enum {
   MOEQ_EDEVICE = -7     /* a HIP call failed                                         */
 };
 
-enum { MOEQ_FMT_NF4 = 1, MOEQ_FMT_INT8_ROWWISE = 2 };
+enum { MOEQ_FMT_NF4 = 1, MOEQ_FMT_INT8_ROWWISE = 2, MOEQ_FMT_NF4_DQ = 3 };
 
 /*
  * A quantized expert tensor [E][rows][cols] in caller-owned device memory.
@@ -65,8 +67,22 @@ enum { MOEQ_FMT_NF4 = 1, MOEQ_FMT_INT8_ROWWISE = 2 };
  * row-wise int8 parametrization):
  *   qdata  int8 [E][rows][cols], codes in [-127, 127].
  *   scales fp32 [E][rows]: absmax(row) / 127.
- * Since blocks never straddle an expert, &qdata[e] / &scales[e] with
- * num_experts = 1 describe expert e alone.
+ * NF4 with double-quantized absmax (format MOEQ_FMT_NF4_DQ, blocksize 64;
+ * bitsandbytes issue #1849, Reproduction: the 4-bit config turns double
+ * quantization on; maintainer thread: per-expert compress_statistics, the
+ * absmax itself quantized, deferred from the first version; the pages fix
+ * no format, this one is the library's own):
+ *   qdata        as for NF4.
+ *   scale_codes  uint8 [E][nb], nb = rows*cols/64: absmax code c of each
+ *                block, c = round_half_even(fp32(fp32(255 a) / m)).
+ *   scales       fp32 [E][ceil(nb/256)]: group scale s2 = fp32(m / 255),
+ *                m the largest absmax of the group (groups of MOEQ_DQ_GROUP
+ *                consecutive blocks of one expert, the last one possibly
+ *                shorter; an all-zero group stores s2 = 0 and codes 0).
+ *   The weights decode with absmax' = fp32(c * s2).
+ * Since blocks and groups never straddle an expert, &qdata[e] / &scales[e]
+ * (and &scale_codes[e]) with num_experts = 1 describe expert e alone.
+ * scale_codes must be NULL for the other formats.
  */
 typedef struct moeq_qweight {
   int32_t format;
@@ -76,6 +92,7 @@ typedef struct moeq_qweight {
   int32_t blocksize;
   void *qdata;
   float *scales;
+  uint8_t *scale_codes;
 } moeq_qweight;
 
 /* Version of this ABI (MOEQ_ABI_VERSION). */
@@ -97,10 +114,13 @@ moeq_status moeq_nf4_codebook(float *out);
  * Quantize-on-load, 4-bit ("MoE Expert Quantization", intro and
  * Implementation details; bitsandbytes issue #1849, maintainer thread).
  * w_bf16: bf16 [E][rows][cols] (16-byte aligned); dst describes the output
- * and must have format MOEQ_FMT_NF4, blocksize 64, cols % 64 == 0, and
- * 16-byte aligned qdata/scales.  For each 64-block: absmax = max |w|;
- * n = fp32(w / absmax) (IEEE division); code = nearest NF4 level, an exact
- * tie to the lower index; an all-zero block stores absmax 0 and code 7.
+ * and must have format MOEQ_FMT_NF4 or MOEQ_FMT_NF4_DQ, blocksize 64,
+ * cols % 64 == 0, and 16-byte aligned qdata/scales/scale_codes.  For each
+ * 64-block: absmax = max |w|; n = fp32(w / absmax) (IEEE division); code =
+ * nearest NF4 level, an exact tie to the lower index; an all-zero block
+ * stores absmax 0 and code 7.  With MOEQ_FMT_NF4_DQ the absmax is then
+ * double-quantized in the same pass (as moeq_compress_absmax would); the
+ * 4-bit codes are those of the plain format.
  * The source may be freed (stream-ordered) as soon as the call returns.
  * Preconditions not checked on device: finite weights.
  */
@@ -117,12 +137,23 @@ moeq_status moeq_quantize_nf4(const uint16_t *w_bf16, const moeq_qweight *dst, v
 moeq_status moeq_quantize_int8_rowwise(const uint16_t *w_bf16, const moeq_qweight *dst, void *stream);
 
 /*
+ * Double-quantize the absmax of an NF4 tensor (bitsandbytes issue #1849,
+ * Reproduction and maintainer thread: double quantization, the absmax
+ * itself quantized).  src: MOEQ_FMT_NF4; dst: MOEQ_FMT_NF4_DQ of the same
+ * shape.  dst->qdata may be src->qdata (the 4-bit codes are shared) or
+ * another buffer (they are copied).  Codes and group scales as described
+ * at moeq_qweight.  Preconditions not checked on device: finite absmax >= 0.
+ */
+moeq_status moeq_compress_absmax(const moeq_qweight *src, const moeq_qweight *dst, void *stream);
+
+/*
  * Dequantize (bitsandbytes issue #1849, maintainer thread: the
  * correctness-first path dequantizes the experts; "MoE Expert
  * Quantization", Implementation details: int8 is dequantized for the
  * forward).  out_bf16: bf16 [E][rows][cols], 16-byte aligned.
  * NF4: out = bf16_rne(fp32(level[code] * absmax)); int8: out =
  * bf16_rne(fp32(q * scale)) -- the fp32 product first, then round to bf16.
+ * NF4 with double-quantized absmax: as NF4 with absmax' = fp32(c * s2).
  */
 moeq_status moeq_dequantize(const moeq_qweight *src, uint16_t *out_bf16, void *stream);
 
@@ -144,7 +175,8 @@ size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qwe
  *                 contribute nothing; a repeated expert counts per occurrence
  *   top_k_weights fp32 [T][K], used as given
  *   gate_up       [E][2I][H]: rows 0..I-1 are the gate, rows I..2I-1 the up
- *                 projection; down [E][H][I]; both NF4 or both int8
+ *                 projection; down [E][H][I]; both of one format (NF4,
+ *                 NF4 with double-quantized absmax, or int8)
  *   out_bf16      bf16 [T][H]:
  *                 out[t] = sum_k w[t,k] * down[e] @ (silu(gate[e] x_t) * up[e] x_t)
  *                 with the k terms added in order k = 0..K-1 (deterministic,
@@ -233,7 +265,8 @@ moeq_status moeq_router_topk(const uint16_t *hidden_bf16, const uint16_t *gate_b
  * live in pinned host memory, one layer is resident and layer N+1 is
  * prefetched on a side stream during layer N (Axolotl issue #3787, Proposed
  * shape; Evidence: the forward is bit-identical with offload on or off).
- * src and dst must describe the same format and shape; their pointers may be
+ * src and dst must describe the same format and shape (codes, scales and,
+ * for MOEQ_FMT_NF4_DQ, absmax codes are copied); their pointers may be
  * pinned host memory (allocated pinned, e.g. hipHostMalloc) or device
  * memory.  The copy is ordered on `stream` like any other call; the caller
  * makes the compute stream wait (an event) before using dst.

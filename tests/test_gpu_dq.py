@@ -1,0 +1,145 @@
+"""GPU parity for NF4 with double-quantized absmax: the quantize, compress and
+dequantize kernels bit-exact against oracle.dq / oracle.nf4, and the forward
+and backward from the double-quantized storage against the fp64 oracle on
+the oracle's dequantized weights (relative Frobenius <= 5e-3), plus bit
+identity with the plain-NF4 path fed the decoded absmax."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantization_moeq_amd as moeq
+import moeq_synth as syn
+from oracle.backward import experts_backward
+from oracle.bf16 import bf16_to_f32
+from oracle.dq import dq_compress, dq_decompress, nf4_dq_dequantize
+from oracle.forward import experts_forward, rel_frobenius
+from oracle.nf4 import nf4_quantize
+from tests.gpu_common import dev_bf16, host, host_bits, require_native, say
+from tests.oracle_lazy import LazyDequant
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _native():
+    require_native()
+
+
+def _weights(shape, seed, zero_expert_rows=0):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    # scale rows so that absmax spans a wide range inside a group
+    w *= np.exp(rng.uniform(-3, 3, size=shape[:2] + (1,))).astype(np.float32)
+    if zero_expert_rows:
+        w[0, :zero_expert_rows] = 0.0        # zero blocks (and whole zero groups)
+    return syn.bf16_bits(torch.from_numpy(w).to(torch.bfloat16))
+
+
+# (E, rows, cols): blocks per expert 8 (one short group, expert 0 all zero),
+# 120, 256 (one exact group), 704 (two groups + a ragged one), 1440
+QSHAPES = [(2, 4, 128), (3, 40, 192), (2, 256, 64), (2, 64, 704), (1, 80, 1152)]
+
+
+@pytest.mark.parametrize("shape", QSHAPES)
+def test_quantize_compress_dequantize_bit_exact(shape):
+    E, R, C = shape
+    bits = _weights(shape, seed=R + C, zero_expert_rows=min(R, 32))
+    say(f"dq quantize shape={shape}")
+    w = dev_bf16(bits)
+    q_dq = moeq.moeq_quantize_nf4(w, double_quant=True)
+    q_nf4 = moeq.moeq_quantize_nf4(w)
+    shared = moeq.moeq_compress_absmax(q_nf4)
+    copied = moeq.moeq_compress_absmax(q_nf4, share_codes=False)
+    deq = moeq.moeq_dequantize(q_dq)
+    torch.cuda.synchronize()
+    ref_q, ref_absmax = nf4_quantize(bits)
+    ref_c, ref_s2 = dq_compress(ref_absmax)
+    for q in (q_dq, shared, copied):
+        np.testing.assert_array_equal(host(q.qdata), ref_q)
+        np.testing.assert_array_equal(host(q.scale_codes), ref_c)
+        np.testing.assert_array_equal(host(q.scales).view(np.uint32), ref_s2.view(np.uint32))
+    assert shared.qdata.data_ptr() == q_nf4.qdata.data_ptr()
+    assert copied.qdata.data_ptr() != q_nf4.qdata.data_ptr()
+    np.testing.assert_array_equal(host_bits(deq), nf4_dq_dequantize(ref_q, ref_c, ref_s2))
+    # storage: 4-bit codes + one byte per block + 4 bytes per group
+    nb = R * C // 64
+    assert q_dq.nbytes() == E * (R * C // 2 + nb + 4 * ((nb + 255) // 256))
+
+
+def _layer(name, T):
+    s = syn.SHAPES[name]
+    gu, dn, x, idx, wts = syn.layer_inputs(s, T, device="cuda")
+    return s, gu, dn, x, idx, wts
+
+
+def _decoded_nf4(qdq):
+    """The plain-NF4 twin of a double-quantized tensor: the same codes with
+    the absmax the oracle decodes (fp32(c * s2)) as fp32 scales."""
+    absmax = dq_decompress(host(qdq.scale_codes), host(qdq.scales))
+    return moeq.QWeight(moeq.FMT_NF4, *qdq.shape, qdq.qdata, torch.from_numpy(absmax).cuda())
+
+
+# (shape, T, sampled tokens, sampled output columns or None): decode and tiled paths
+FWD = [("tiny", 64, 64, None), ("olmoe", 1, 1, None), ("olmoe", 32, 2, None), ("olmoe", 4096, 2, 512),
+       ("qwen3", 8192, 1, 256)]
+
+
+@pytest.mark.parametrize("name,T,ns,nc", FWD)
+def test_forward_double_quant(name, T, ns, nc):
+    s, gu, dn, x, idx, wts = _layer(name, T)
+    say(f"dq forward {name} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu, double_quant=True), moeq.moeq_quantize_nf4(dn, double_quant=True)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    twin = moeq.moeq_experts_forward(x, idx, wts, _decoded_nf4(qg), _decoded_nf4(qd))
+    torch.cuda.synchronize()
+    # the in-kernel absmax decode is exactly the plain path on decoded absmax
+    assert torch.equal(out.view(torch.int16), twin.view(torch.int16))
+    rng = np.random.default_rng(T)
+    tokens = np.arange(T) if ns >= T else np.sort(rng.choice(T, ns, replace=False))
+    cols = None if nc is None else np.sort(rng.choice(s.H, nc, replace=False))
+    rows = None if cols is None else torch.from_numpy(cols).cuda()
+    ref = experts_forward(host_bits(x)[tokens], host(idx)[tokens], host(wts)[tokens], LazyDequant(gu, "nf4_dq"),
+                          LazyDequant(dn, "nf4_dq", rows=rows))
+    got = bf16_to_f32(host_bits(out)[tokens]).astype(np.float64)
+    if cols is not None:
+        got = got[:, cols]
+    err = rel_frobenius(got, ref)
+    print(f"dq {name} T={T}: rel Frobenius error {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name,T,ns", [("tiny", 64, 64), ("olmoe", 1024, 2)])
+def test_backward_double_quant(name, T, ns):
+    s, gu, dn, x, idx, wts = _layer(name, T)
+    dout = syn.grad_output(T, s.H, device="cuda")
+    say(f"dq backward {name} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu, double_quant=True), moeq.moeq_quantize_nf4(dn, double_quant=True)
+    gx, gw = moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout)
+    tx, tw = moeq.moeq_experts_backward(x, idx, wts, _decoded_nf4(qg), _decoded_nf4(qd), dout)
+    torch.cuda.synchronize()
+    assert torch.equal(gx.view(torch.int16), tx.view(torch.int16))
+    assert torch.equal(gw, tw)
+    rng = np.random.default_rng(T + 1)
+    tokens = np.arange(T) if ns >= T else np.sort(rng.choice(T, ns, replace=False))
+    ref_x, ref_w = experts_backward(host_bits(x)[tokens], host(idx)[tokens], host(wts)[tokens],
+                                    LazyDequant(gu, "nf4_dq"), LazyDequant(dn, "nf4_dq"), host_bits(dout)[tokens])
+    ex = rel_frobenius(bf16_to_f32(host_bits(gx)[tokens]).astype(np.float64), ref_x)
+    ew = rel_frobenius(host(gw)[tokens].astype(np.float64), ref_w)
+    print(f"dq backward {name} T={T}: grad_hidden {ex:.3e}, grad_weights {ew:.3e}")
+    assert ex <= TOL and ew <= TOL
+
+
+def test_copy_async_carries_absmax_codes():
+    s = syn.SHAPES["tiny"]
+    gu = syn.expert_weights(s.gate_up_shape, device="cuda")
+    say("dq copy_async round trip")
+    q = moeq.moeq_quantize_nf4(gu, double_quant=True)
+    hostq = q.like("cpu", pin_memory=True)
+    moeq.moeq_qweight_copy_async(q, hostq)
+    back = q.like("cuda")
+    moeq.moeq_qweight_copy_async(hostq, back)
+    torch.cuda.synchronize()
+    for a, b in zip(q._tensors(), back._tensors()):
+        assert torch.equal(a, b)

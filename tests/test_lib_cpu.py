@@ -35,7 +35,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert moeq.moeq_abi_version() == 1
+    assert moeq.moeq_abi_version() == 2
     for s in range(0, -8, -1):
         assert moeq.moeq_status_string(s) != "unknown status"
     assert moeq.moeq_status_string(-99) == "unknown status"
@@ -72,8 +72,8 @@ def test_kernel_bucket_layout_assumption():
     assert np.min(np.abs(pos - np.round(pos))) / 16.0 > 1e-3
 
 
-def _qw(fmt=1, E=1, R=4, C=64, bs=64, q=256, s=512):
-    return moeq._QW(fmt, E, R, C, bs, q, s)
+def _qw(fmt=1, E=1, R=4, C=64, bs=64, q=256, s=512, c=None):
+    return moeq._QW(fmt, E, R, C, bs, q, s, c)
 
 
 def _quant(qw, w=4096):
@@ -125,3 +125,28 @@ def test_forward_validation_and_workspace_sizing():
     assert fwd(10, 2, gu, dn, ws_ptr=0) == -6
     assert fwd(10, 2, gu, dn, x=4100) == -5
     assert lib.moeq_route_workspace_bytes(10, 2, 5000) == 0
+
+
+def test_double_quant_validation_rejects_before_any_device_call():
+    lib = moeq._load()
+    P = ctypes.c_void_p
+    dq = _qw(fmt=3, c=1024)
+    assert _quant(_qw(fmt=3)) == -1                      # NF4_DQ without absmax codes
+    assert _quant(_qw(fmt=1, c=1024)) == -1              # absmax codes on plain NF4
+    assert _quant(_qw(fmt=3, c=1032)) == -5              # misaligned absmax codes
+    assert _quant(_qw(fmt=3, C=96, c=1024)) == -3
+    assert lib.moeq_dequantize(ctypes.byref(_qw(fmt=3)), P(4096), None) == -1
+
+    def comp(src, dst):
+        return lib.moeq_compress_absmax(ctypes.byref(src), ctypes.byref(dst), None)
+
+    assert comp(_qw(fmt=2, C=64, bs=64), dq) == -4       # source must be plain NF4
+    assert comp(_qw(), _qw()) == -4                      # destination must be NF4_DQ
+    assert comp(_qw(R=8), dq) == -2                      # shapes differ
+    assert comp(_qw(), _qw(fmt=3)) == -1
+    assert lib.moeq_compress_absmax(None, ctypes.byref(dq), None) == -1
+    # the forward takes NF4_DQ pairs, not a mix with plain NF4
+    E, H, I = 4, 128, 64
+    gu, dn = _qw(3, E, 2 * I, H, 64, c=1024), _qw(3, E, H, I, 64, c=2048)
+    assert lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(dn)) > 0
+    assert lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(_qw(1, E, H, I, 64))) == 0
