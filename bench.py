@@ -17,7 +17,9 @@ kernel of the step, from the stage events recorded on every other timed step;
 HBM; ``backward`` = the gradients through the frozen packed experts for the
 same batch; ``router`` = the router front-end (gate GEMM, softmax, top-K)
 on the same batch; ``offload`` = the forward with the packed experts in
-pinned host memory and the next layer prefetched; ``codec`` = row-wise int8 quantize and the two dequantizes;
+pinned host memory and the next layer prefetched; ``double_quant`` = the
+same quantize, forward, decode and backward with double-quantized absmax;
+``codec`` = row-wise int8 quantize and the two dequantizes;
 ``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
@@ -37,6 +39,9 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 NF4_BYTES_PER_ELEM = 2.0 + 0.5 + 4.0 / 64   # bf16 read + packed code + absmax share
 NF4_PACKED_BYTES_PER_ELEM = 0.5 + 4.0 / 64  # what the forward streams per weight element
+# NF4 with double-quantized absmax: one code byte per 64-block, 4 bytes per 256 blocks
+DQ_PACKED_BYTES_PER_ELEM = 0.5 + 1.0 / 64 + 4.0 / (64 * 256)
+DQ_BYTES_PER_ELEM = 2.0 + DQ_PACKED_BYTES_PER_ELEM
 
 
 def parse():
@@ -52,14 +57,15 @@ def parse():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-offload", action="store_true")
+    ap.add_argument("--no-double-quant", action="store_true")
     return ap.parse_args()
 
 
-def forward_bytes_flops(s, idx_np, T):
+def forward_bytes_flops(s, idx_np, T, packed_bpe=NF4_PACKED_BYTES_PER_ELEM):
     """Algorithmic bytes and flops of one forward: touched experts' packed weights
     once, x in and out once, the routing inputs once; 6*T*K*H*I flops."""
     U = len(set(idx_np.reshape(-1).tolist()))
-    wbytes = U * 3 * s.H * s.I * NF4_PACKED_BYTES_PER_ELEM
+    wbytes = U * 3 * s.H * s.I * packed_bpe
     abytes = 2 * T * s.H * 2 + T * s.K * 8
     flops = 6.0 * T * s.K * s.H * s.I
     return wbytes + abytes, flops, U
@@ -154,7 +160,13 @@ def device_copy_GBps(torch, dev, nbytes=1 << 30, reps=10):
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
-def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, calls=48):
+def clone_q(moeq, q):
+    t = [u.clone() for u in q._tensors()]
+    return moeq.QWeight(q.format, q.num_experts, q.rows, q.cols, t[0], t[1], t[2] if len(t) == 3 else None)
+
+
+def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, calls=48,
+                   packed_bpe=NF4_PACKED_BYTES_PER_ELEM):
     """Forward-only figures at T = 1 and 32.  The calls rotate over `layers`
     copies of the quantized layer (together larger than the last-level cache),
     so every call streams its experts' codes from HBM as in a many-layer model;
@@ -162,8 +174,7 @@ def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, ca
     with stage events gives the per-kernel split."""
     stack = [(qg, qd)]
     for _ in range(layers - 1):
-        c = lambda q: moeq.QWeight(q.format, q.num_experts, q.rows, q.cols, q.qdata.clone(), q.scales.clone())
-        stack.append((c(qg), c(qd)))
+        stack.append((clone_q(moeq, qg), clone_q(moeq, qd)))
     dec = {}
     for Td in (1, 32):
         xd = syn.hidden_states(Td, s.H, device=dev, layer=1)
@@ -190,7 +201,7 @@ def decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps, layers=4, ca
         torch.cuda.synchronize()
         kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evd[layers:]]))
                for j, n in enumerate(["route", "g1_gate_up_swiglu", "g2_down", "combine"])}
-        nb, fl, Ud = forward_bytes_flops(s, idd.cpu().numpy(), Td)
+        nb, fl, Ud = forward_bytes_flops(s, idd.cpu().numpy(), Td, packed_bpe)
         dec[f"T{Td}"] = {"tokens_per_s": Td / (tms * 1e-3), "forward_ms": tms,
                          "packed_GBps": nb / (tms * 1e-3) / 1e9,
                          "hbm_frac": nb / (tms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -289,6 +300,45 @@ def offload_figures(torch, np, moeq, s, qg, qd, x, idx, wts, dev, fwd_ms, layers
             "layer_bytes": nbytes, "copy_ms": copy_ms, "copy_GBps": nbytes / (copy_ms * 1e-3) / 1e9,
             "resident_forward_ms": fwd_ms, "offloaded_forward_ms": off_ms,
             "overlap": (fwd_ms + copy_ms - off_ms) / min(fwd_ms, copy_ms)}
+
+
+def double_quant_figures(torch, np, moeq, syn, s, gu, dn, x, idx, wts, dev, copy_GBps, reps=10):
+    """The same layer with double-quantized absmax: quantize-on-load into that
+    format, the T-token forward, the decode forwards and the backward, each
+    decoding the absmax inside its kernels; plus the storage of both formats."""
+    qg = moeq.QWeight.empty(moeq.FMT_NF4_DQ, *s.gate_up_shape, device=dev)
+    qd = moeq.QWeight.empty(moeq.FMT_NF4_DQ, *s.down_shape, device=dev)
+    T = x.shape[0]
+    out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    q_ms = timed(lambda: (moeq.moeq_quantize_nf4(gu, out=qg), moeq.moeq_quantize_nf4(dn, out=qd)))
+    nel = gu.numel() + dn.numel()
+    qb = nel * DQ_BYTES_PER_ELEM
+    f_ms = timed(lambda: moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=out, workspace=ws))
+    nf4_bytes = nel * NF4_PACKED_BYTES_PER_ELEM
+    return {"workload": "same layer and batch, absmax double-quantized (8-bit code per block, fp32 per 256 blocks)",
+            "quantize_ms": q_ms, "quantize_GBps": qb / (q_ms * 1e-3) / 1e9,
+            "quantize_hbm_frac": qb / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "quantize_copy_frac": qb / (q_ms * 1e-3) / 1e9 / copy_GBps,
+            "forward_ms": f_ms, "tokens_per_s": T / (f_ms * 1e-3),
+            "decode": decode_figures(torch, np, moeq, syn, s, qg, qd, dev, copy_GBps,
+                                     packed_bpe=DQ_PACKED_BYTES_PER_ELEM),
+            "backward": backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev),
+            "layer_bytes": {"nf4": nf4_bytes, "nf4_double_quant": float(qg.nbytes() + qd.nbytes()),
+                            "bits_per_weight_nf4": 8 * NF4_PACKED_BYTES_PER_ELEM,
+                            "bits_per_weight_double_quant": 8.0 * (qg.nbytes() + qd.nbytes()) / nel}}
 
 
 def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
@@ -475,6 +525,8 @@ def main():
         result["router"] = router_figures(torch, np, moeq, syn, s, x, dev, copy_GBps)
     if not args.no_backward:
         result["backward"] = backward_figures(torch, np, moeq, syn, s, qg, qd, x, idx, wts, dev)
+    if not args.no_double_quant:
+        result["double_quant"] = double_quant_figures(torch, np, moeq, syn, s, gu, dn, x, idx, wts, dev, copy_GBps)
     if not args.no_codec:
         result["codec"] = codec_figures(torch, np, moeq, syn, dev, copy_GBps)
 

@@ -40,7 +40,10 @@
 //     registers one K step ahead and dequantizes them in registers into the
 //     MFMA A operand -- the weights never touch LDS.  The dequantized value is
 //     exactly bf16_rne(fp32(level * absmax)) / bf16_rne(fp32(q * scale)), the
-//     same bits moeq_dequantize writes.
+//     same bits moeq_dequantize writes.  With double-quantized absmax the
+//     lane loads the block's 8-bit absmax code and its group's scale instead
+//     and forms fp32(code * scale) when the step is consumed (bitsandbytes
+//     issue #1849, Reproduction and maintainer thread: double quantization).
 //   * K is permuted inside each K step (the GEMM does not care which k each
 //     MFMA lane slot holds, as long as both operands agree): lane half h of
 //     every MFMA covers one whole 64-wide NF4 block of its row, so one absmax

@@ -37,6 +37,7 @@ Modules:
 * :mod:`oracle.forward` -- the routed experts forward in fp64.
 * :mod:`oracle.backward` -- its gradients with respect to the hidden states
   and the routing weights (frozen weights), in fp64.
+* :mod:`oracle.router`  -- the router front-end (logits, softmax, top-K) in fp64.
 * :mod:`oracle.dq`      -- double quantization of the NF4 absmax (8-bit codes
   per 256-block group of one expert, fp32 group scales).
 
