@@ -169,6 +169,14 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Anchors for hand-placed VALU work: pin_in makes x look redefined here
+// and pin_out makes it look used here (both emit nothing).  Work between a
+// stage's pin_in of its inputs and pin_out of its results stays between the
+// two points, in program order with the fences around it.
+__device__ __forceinline__ void pin_in(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_in(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_out(uint32_t x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(bf16x8, v);
@@ -224,6 +232,44 @@ __device__ __forceinline__ bf16x8 nf4_frag(const Nf4Table& t, uint32_t w) {
   return as_bf16x8(perm(h03, l03, 0x05010400u), perm(h03, l03, 0x07030602u), perm(h47, l47, 0x05010400u),
                    perm(h47, l47, 0x07030602u));
 }
+
+// nf4_frag in four stages of 6 to 8 VALU instructions, so that a GEMM can
+// slot one stage between two MFMAs (an MFMA runs for 32 cycles while the
+// same wave keeps issuing independent VALU work).  Same arithmetic, same bits.
+struct Nf4FragStages {
+  static constexpr int kStages = 4;
+  uint32_t w, me, mo, se, so, le, he, lo, ho, r[4];
+  __device__ __forceinline__ void stage(int k, const Nf4Table& t) {
+    if (k == 0) {
+      pin_in(w);
+      me = perm(w, w << 8, 0x0B090A08u);
+      mo = perm(w << 4, w << 12, 0x0B090A08u);
+      se = (w >> 4) & 0x07070707u;
+      so = w & 0x07070707u;
+      pin_out(me), pin_out(mo), pin_out(se), pin_out(so);
+    } else if (k == 1) {
+      pin_in(me), pin_in(se);
+      le = (me & perm(t.lo[3], t.lo[2], se)) | (~me & perm(t.lo[1], t.lo[0], se));
+      he = (me & perm(t.hi[3], t.hi[2], se)) | (~me & perm(t.hi[1], t.hi[0], se));
+      pin_out(le), pin_out(he);
+    } else if (k == 2) {
+      pin_in(mo), pin_in(so);
+      lo = (mo & perm(t.lo[3], t.lo[2], so)) | (~mo & perm(t.lo[1], t.lo[0], so));
+      ho = (mo & perm(t.hi[3], t.hi[2], so)) | (~mo & perm(t.hi[1], t.hi[0], so));
+      pin_out(lo), pin_out(ho);
+    } else {
+      pin_in(le), pin_in(he), pin_in(lo), pin_in(ho);
+      const uint32_t l03 = perm(lo, le, 0x05010400u), h03 = perm(ho, he, 0x05010400u);
+      const uint32_t l47 = perm(lo, le, 0x07030602u), h47 = perm(ho, he, 0x07030602u);
+      r[0] = perm(h03, l03, 0x05010400u);
+      r[1] = perm(h03, l03, 0x07030602u);
+      r[2] = perm(h47, l47, 0x05010400u);
+      r[3] = perm(h47, l47, 0x07030602u);
+      pin_out(r[0]), pin_out(r[1]), pin_out(r[2]), pin_out(r[3]);
+    }
+  }
+  __device__ __forceinline__ bf16x8 value() const { return as_bf16x8(r[0], r[1], r[2], r[3]); }
+};
 
 // ---------------------------------------------------------------------------
 // int8 dequantization in registers: bf16_rne(fp32(q * s)).  q + 128 is the
@@ -316,8 +362,32 @@ template <int FMT>
 struct Dequant {  // NF4, plain or with double-quantized absmax
   Nf4Table t;
   __device__ __forceinline__ void prepare(const RowCodes<FMT>& r) { t = nf4_table(r.scale.value()); }
+  // the same table in kPrepStages pieces: piece q holds levels 4q .. 4q+3
+  static constexpr int kPrepStages = 4;
+  __device__ __forceinline__ void prep_stage(int q, const RowCodes<FMT>& r) {
+    float a = r.scale.value();
+    pin_in(a);
+    const uint32_t p0 = pack_bf16x2(__uint_as_float(kNf4LevelBits[4 * q]) * a,
+                                    __uint_as_float(kNf4LevelBits[4 * q + 1]) * a);
+    const uint32_t p1 = pack_bf16x2(__uint_as_float(kNf4LevelBits[4 * q + 2]) * a,
+                                    __uint_as_float(kNf4LevelBits[4 * q + 3]) * a);
+    t.lo[q] = perm(p1, p0, 0x06040200u);
+    t.hi[q] = perm(p1, p0, 0x07050301u);
+    pin_out(t.lo[q]), pin_out(t.hi[q]);
+  }
   // MFMA step s (0..7) of the K step: codes word s = 8 consecutive k of the block
   __device__ __forceinline__ bf16x8 frag(const RowCodes<FMT>& r, int s) const { return nf4_frag(t, r.word(s)); }
+};
+
+// One A fragment computed in stages: begin() takes MFMA step s's codes,
+// stage(k) for k = 0 .. kStages-1 in order, then value().
+template <int FMT>
+struct FragStages {  // NF4, plain or with double-quantized absmax
+  static constexpr int kStages = Nf4FragStages::kStages;
+  Nf4FragStages f;
+  __device__ __forceinline__ void begin(const RowCodes<FMT>& r, int s) { f.w = r.word(s); }
+  __device__ __forceinline__ void stage(int k, const Dequant<FMT>& d) { f.stage(k, d.t); }
+  __device__ __forceinline__ bf16x8 value() const { return f.value(); }
 };
 
 template <>
@@ -327,10 +397,34 @@ struct Dequant<MOEQ_FMT_INT8_ROWWISE> {
     s = r.scale.value();
     ns128 = -128.0f * s;
   }
+  static constexpr int kPrepStages = 1;
+  __device__ __forceinline__ void prep_stage(int, const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r) { prepare(r); }
   // MFMA step s (0..3): 8 consecutive int8 codes = words 2s, 2s+1
   __device__ __forceinline__ bf16x8 frag(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r, int s_) const {
     return i8_frag(r.word(2 * s_), r.word(2 * s_ + 1), s, ns128);
   }
+};
+
+// i8_frag in two stages (one code word each), same arithmetic.
+template <>
+struct FragStages<MOEQ_FMT_INT8_ROWWISE> {
+  static constexpr int kStages = 2;
+  uint32_t w[2], r[4];
+  __device__ __forceinline__ void begin(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& c, int s) {
+    w[0] = c.word(2 * s);
+    w[1] = c.word(2 * s + 1);
+  }
+  __device__ __forceinline__ void stage(int k, const Dequant<MOEQ_FMT_INT8_ROWWISE>& d) {
+    pin_in(w[k]);
+    const uint32_t u = w[k] ^ 0x80808080u;
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __builtin_fmaf((float)((u >> (8 * j)) & 0xffu), d.s, d.ns128);
+    r[2 * k] = pack_bf16x2(f[0], f[1]);
+    r[2 * k + 1] = pack_bf16x2(f[2], f[3]);
+    pin_out(r[2 * k]), pin_out(r[2 * k + 1]);
+  }
+  __device__ __forceinline__ bf16x8 value() const { return as_bf16x8(r[0], r[1], r[2], r[3]); }
 };
 
 // ---------------------------------------------------------------------------
@@ -417,122 +511,165 @@ struct Core {
     const int chunk = (lane % kCpr) ^ swz(staged_row(wave, lane, 0));
     char* stage0 = sX + staged_row(wave, 0, 0) * kCpr * 16;
 
-    auto stage = [&](int k0, int buf) {
+    // instruction i of the token DMA for K offset k0 into buffer buf
+    auto stage_one = [&](int k0, int buf, int i) {
       int kk = k0 + 8 * chunk;
       kk = kk < K ? kk : 0;
+      __builtin_amdgcn_global_load_lds(tbase + roff[i] + 2 * kk,
+                                       stage0 + buf * buf_bytes + i * kWaves * kRpi * kCpr * 16, 16, 0, 0);
+    };
+    auto stage = [&](int k0, int buf) {
 #pragma unroll
-      for (int i = 0; i < kInstr; ++i) {
-        __builtin_amdgcn_global_load_lds(tbase + roff[i] + 2 * kk,
-                                         stage0 + buf * buf_bytes + i * kWaves * kRpi * kCpr * 16, 16, 0, 0);
-      }
+      for (int i = 0; i < kInstr; ++i) stage_one(k0, buf, i);
     };
 
     // B fragment of token block b at MFMA step s: row 32b + l32, chunk
     // (kCpr/2)*hh + s, stored at slot chunk ^ swz(row) (swz(row) = swz(l32)).
     const int rsw = swz(l32);
 
-    // One K step: start the next step's token DMAs and code loads, run this
-    // step's MFMAs from LDS buffer ks & 1 and the codes in (c0, c1).  A straight
-    // line (no branches around the MFMAs, so the accumulators stay put): a
-    // wave with no weight rows multiplies zeros, and the last step prefetches
-    // a harmless extra step (zero codes, an in-range row).
-    auto kstep = [&](int ks, const RowCodes<FMT>& c0, const RowCodes<FMT>& c1, RowCodes<FMT>& n0,
-                     RowCodes<FMT>& n1) {
-      const int buf = ks % kNbuf;
-      if (kNbuf == 2) {
-        stage((ks + 1) * kStep, (ks + 1) % kNbuf);
-        __builtin_amdgcn_sched_barrier(0);  // the code loads below must issue after the DMAs
-        n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
-        n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
-      } else {
-        n0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
-        n1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
-        __builtin_amdgcn_sched_barrier(0);  // the DMAs below must issue after the code loads
-        stage((ks + 2) * kStep, (ks + 2) % kNbuf);
-      }
+    // Registers of one K step: the packed codes of the lane's two weight
+    // rows, their dequantization tables and the A fragments of MFMA step 0.
+    struct StepRegs {
+      RowCodes<FMT> c0, c1;
       Dequant<FMT> d0, d1;
-      d0.prepare(c0);
-      d1.prepare(c1);
+      bf16x8 a0, a1;
+    };
+
+    // One K step.  Runs this step's MFMAs from LDS buffer ks % kNbuf with
+    // the registers in `cur`, and meanwhile
+    //   * loads step ks + 1's codes into `nxt` (first thing in the step),
+    //   * starts the token DMAs of step ks + 1 (two buffers) or ks + 2
+    //     (three), spread over the first kDmaSub MFMA steps (a burst at the
+    //     step start stalls the wave on the memory pipeline),
+    //   * dequantizes MFMA step s + 1's A fragments during MFMA step s, and
+    //     during the last MFMA step builds step ks + 1's tables and its first
+    //     A fragments, so the next step starts on MFMAs right after the
+    //     barrier.
+    // The VALU work is cut into stages of a few instructions and one slice is
+    // placed after each MFMA, fenced so the compiler keeps it there (an MFMA
+    // runs for 32 cycles while the wave keeps issuing independent VALU work;
+    // left to itself the compiler bunches the VALU work between MFMA bursts).
+    // A straight line (no branches around the MFMAs, so the accumulators stay
+    // put): a wave with no weight rows multiplies zeros, and the last step
+    // prefetches a harmless extra step (zero codes, an in-range row).
+    constexpr int kS = kStep / 16;         // MFMA steps per K step
+    constexpr int kSlots = 2 * NB;         // MFMAs per MFMA step
+    constexpr int kDmaSub = kS / 2;        // MFMA steps that carry the DMAs
+    constexpr int kFragWork = 2 * FragStages<FMT>::kStages;
+    constexpr int kPrepWork = 2 * Dequant<FMT>::kPrepStages;
+    constexpr int kLastWork = kPrepWork + kFragWork;
+    auto kstep = [&](int ks, StepRegs& cur, StepRegs& nxt) {
+      const int buf = ks % kNbuf;
+      const int dstep = kNbuf == 2 ? ks + 1 : ks + 2;  // the step the DMAs fetch
       const char* xb = sX + buf * buf_bytes + l32 * kCpr * 16;
       auto bfrag = [&](int s_, int b) {
         const int slot = ((kCpr / 2) * hh + s_) ^ rsw;
         return *reinterpret_cast<const bf16x8*>(xb + (32 * b * kCpr + slot) * 16);
       };
-      // Software pipeline over the MFMA steps of the K step: while step s's
-      // 2*NB MFMAs run, the B fragments of step s+1 are read from LDS and its
-      // A fragments are dequantized.
-      constexpr int kS = kStep / 16;
-      bf16x8 a0 = d0.frag(c0, 0), a1 = d1.frag(c1, 0);
+      nxt.c0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
+      nxt.c1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+      __builtin_amdgcn_sched_barrier(0);  // the DMAs below must issue after the code loads
+      bf16x8 a0 = cur.a0, a1 = cur.a1;
       bf16x8 xf[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) xf[b] = bfrag(0, b);
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
-        bf16x8 xn[NB], a0n, a1n;
-        if (s + 1 < kS) {
+        const bool last = s + 1 == kS;
+        FragStages<FMT> f0, f1;
+        if (!last) {
+          f0.begin(cur.c0, s + 1);
+          f1.begin(cur.c1, s + 1);
+        }
+        if (s < kDmaSub) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) xn[b] = bfrag(s + 1, b);
-          a0n = d0.frag(c0, s + 1);
-          a1n = d1.frag(c1, s + 1);
+          for (int i = s * kInstr / kDmaSub; i < (s + 1) * kInstr / kDmaSub; ++i)
+            stage_one(dstep * kStep, dstep % kNbuf, i);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          acc0[b] = mfma(a0, xf[b], acc0[b]);
-          acc1[b] = mfma(a1, xf[b], acc1[b]);
-        }
-        if (s + 1 < kS) {
-          // interleave: the next B-fragment reads between the first MFMAs,
-          // then the next A-fragment dequantization between the rest
+        for (int i = 0; i < kSlots; ++i) {
+          const int b = i >> 1;
+          if (i & 1)
+            acc1[b] = mfma(a1, xf[b], acc1[b]);
+          else
+            acc0[b] = mfma(a0, xf[b], acc0[b]);
+          if (!last) {
+            // token block b is done for this MFMA step: read its next fragment
+            if (i & 1) xf[b] = bfrag(s + 1, b);
+            // frag stages j in [i*W/kSlots, (i+1)*W/kSlots): f0's, then f1's
+            constexpr int kF = FragStages<FMT>::kStages;
 #pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            for (int j = i * kFragWork / kSlots; j < (i + 1) * kFragWork / kSlots; ++j) {
+              if (j >= kF)
+                f1.stage(j - kF, cur.d1);
+              else
+                f0.stage(j, cur.d0);
+            }
+          } else {
+            // next K step: its two tables first, then its first A fragments
+#pragma unroll
+            for (int j = i * kLastWork / kSlots; j < (i + 1) * kLastWork / kSlots; ++j) {
+              if (j < kPrepWork) {
+                if (j & 1)
+                  nxt.d1.prep_stage(j >> 1, nxt.c1);
+                else
+                  nxt.d0.prep_stage(j >> 1, nxt.c0);
+              } else {
+                const int k = j - kPrepWork;
+                constexpr int kF = FragStages<FMT>::kStages;
+                if (k == 0) f0.begin(nxt.c0, 0);
+                if (k == kF) f1.begin(nxt.c1, 0);
+                if (k >= kF)
+                  f1.stage(k - kF, nxt.d1);
+                else
+                  f0.stage(k, nxt.d0);
+              }
+            }
           }
-#pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 64 / NB, 0);  // VALU
-          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) xf[b] = xn[b];
-        a0 = a0n;
-        a1 = a1n;
+        if (!last) {
+          a0 = f0.value();
+          a1 = f1.value();
+        } else {
+          nxt.a0 = f0.value();
+          nxt.a1 = f1.value();
+        }
       }
-      // Vector loads complete in order: once at most the loads issued in this
-      // step are outstanding (2*kLoads code loads, plus with three buffers
-      // the DMAs two steps ahead), this thread's DMAs for step ks + 1 have
-      // landed in LDS; the rest keep flying across the barrier.  No release
-      // fence is needed: every LDS read of this step has been consumed by an
-      // MFMA above; the acquire fence keeps the next step's LDS reads below
-      // the barrier.
-      __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * RowCodes<FMT>::kLoads + (kNbuf == 3 ? kInstr : 0)>);
+      // Vector loads complete in order.  Two buffers: this step's DMAs (for
+      // step ks + 1) are the last loads issued, so wait for all.  Three
+      // buffers: the DMAs for step ks + 1 were issued in the previous step and
+      // only this step's code loads and DMAs may still be in flight.  No
+      // release fence is needed: every LDS read of this step has been
+      // consumed by an MFMA above; the acquire fence keeps the next step's
+      // LDS reads below the barrier.
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<kNbuf == 2 ? 0 : 2 * RowCodes<FMT>::kLoads + kInstr>);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
-    // two register sets for the codes, used in turn (no copies between steps)
-    RowCodes<FMT> ca0, ca1, cb0, cb1;
+    // two register sets, used in turn (no copies between steps)
+    StepRegs ra, rb;
     stage(0, 0);
-    ca0.fetch(q0, s0, 0, hh, K, wave_on);
-    ca1.fetch(q1, s1, 0, hh, K, wave_on);
-    if (kNbuf == 3) {
-      __builtin_amdgcn_sched_barrier(0);
-      stage(kStep, 1);
-      __builtin_amdgcn_s_waitcnt(kVmcntWait<kInstr>);  // step 0 landed; step 1 may still fly
-    } else {
-      __builtin_amdgcn_s_waitcnt(0);
-    }
+    if (kNbuf == 3) stage(kStep, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ra.c0.fetch(q0, s0, 0, hh, K, wave_on);
+    ra.c1.fetch(q1, s1, 0, hh, K, wave_on);
+    __builtin_amdgcn_s_waitcnt(0);
+    ra.d0.prepare(ra.c0);
+    ra.d1.prepare(ra.c1);
+    ra.a0 = ra.d0.frag(ra.c0, 0);
+    ra.a1 = ra.d1.frag(ra.c1, 0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     const int nks = (K + kStep - 1) / kStep;
     int ks = 0;
     for (; ks + 1 < nks; ks += 2) {
-      kstep(ks, ca0, ca1, cb0, cb1);
-      kstep(ks + 1, cb0, cb1, ca0, ca1);
+      kstep(ks, ra, rb);
+      kstep(ks + 1, rb, ra);
     }
-    if (ks < nks) kstep(ks, ca0, ca1, cb0, cb1);
+    if (ks < nks) kstep(ks, ra, rb);
   }
 };
 
