@@ -998,22 +998,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
     // this lane's half of step ks of the token row: K is a multiple of 64,
     // so the half is wholly in range or wholly past the end (then row start)
-    auto load_b = [&](bf16x8 (&xb)[kS], int ks) {
+    // fragment s_ of this lane's half of step ks of the token row: K is a
+    // multiple of 64, so the half is wholly in range or wholly past the end
+    // (then the row start)
+    auto bptr = [&](int ks) {
       const int kb = ks * kStep + (kStep / 2) * hh;
-      const bf16x8* p = reinterpret_cast<const bf16x8*>(brow + (kb < K ? kb : 0));
-#pragma unroll
-      for (int s_ = 0; s_ < kS; ++s_) xb[s_] = p[s_];
+      return reinterpret_cast<const bf16x8*>(brow + (kb < K ? kb : 0));
     };
-    // One K step: issue the next step's token fragments, multiply this
-    // step's, then refill this step's code registers two steps ahead.  Loads
+    // One K step: multiply this step's token fragments, each one replaced
+    // by the next step's as soon as its two MFMAs have issued (one register
+    // set, so the kernel stays within three waves' worth of registers per
+    // SIMD), then refill this step's code registers two steps ahead.  Loads
     // complete in issue order, so codes stay in flight across a step while
     // the token fragments (L2 hits) are awaited.  Steps past the wave's range
     // load in-range addresses and are zeroed through their scale.
-    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, bf16x8 (&xa)[kS], bf16x8 (&xn)[kS]) {
+    bf16x8 xa[kS];
+    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1) {
       // keep each step's arithmetic after the previous step's (hoisting it
       // would wait for codes that are still loading)
       __builtin_amdgcn_sched_barrier(0);
-      load_b(xn, ks + 1);
+      const bf16x8* pn = bptr(ks + 1);
       const RowCodes<FMT> c0 = sc0.use(), c1 = sc1.use();
       Dequant<FMT> d0, d1;
       d0.prepare(c0);
@@ -1022,12 +1026,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       for (int s_ = 0; s_ < kS; ++s_) {
         acc0 = mfma(d0.frag(c0, s_), xa[s_], acc0);
         acc1 = mfma(d1.frag(c1, s_), xa[s_], acc1);
+        xa[s_] = pn[s_];
       }
       sc0.fetch(q0, s0, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs0);
       sc1.fetch(q1, s1, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs1);
     };
-    bf16x8 xa[kS], xb[kS];
-    load_b(xa, ks0);
+    {
+      const bf16x8* p0 = bptr(ks0);
+#pragma unroll
+      for (int s_ = 0; s_ < kS; ++s_) xa[s_] = p0[s_];
+    }
     cb0.fetch(q0, s0, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs0);
     cb1.fetch(q1, s1, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs1);
     // Two steps per trip, register sets alternating, with no branch between
@@ -1037,8 +1045,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     // trailing step past the range: its scale is zero, its A operand exactly
     // zero, and it adds nothing.
     for (int ks = ks0; ks < ks1; ks += 2) {
-      kstep(ks, ca0, ca1, xa, xb);
-      kstep(ks + 1, cb0, cb1, xb, xa);
+      kstep(ks, ca0, ca1);
+      kstep(ks + 1, cb0, cb1);
     }
 
     // the P partial sums of each row block, added in part order
