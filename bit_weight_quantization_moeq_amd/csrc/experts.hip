@@ -15,8 +15,8 @@
 //       pairs gate column j with up column j and writes h = bf16(silu(g) * u).
 //   G2  the same machinery over (expert, up to 256 sorted rows, 256 output
 //       columns): h times the down rows, scaled by the routing weight in fp32
-//       -> y.
-//   C1  out[t] = bf16(sum over k = 0..K-1, in that order, of y[slot[t*K+k]]).
+//       -> y, rounded to bf16 (the model's compute dtype).
+//   C1  out[t] = bf16(fp32 sum over k = 0..K-1, in that order, of y[slot[t*K+k]]).
 //
 // Few-assignment path (n <= 512, decode): no routing kernels and no token
 // tiles; each workgroup finds its expert and that expert's assignments from
@@ -777,10 +777,11 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
 // G2: y[p][n] = w_p * (down_n . h_p) in fp32.  Wave w: output columns
 // ncol = n0 + 64w .. +64 (two 32-row MFMA blocks).
 // ---------------------------------------------------------------------------
-template <int FMT, int NB>
+// Y: float (fp32 y) or uint16_t (y rounded to bf16).
+template <int FMT, int NB, typename Y>
 __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_t* h, int H, int I, int ncol,
                                         bool on, const uint8_t* q0, const SRow<FMT>& s0, const uint8_t* q1,
-                                        const SRow<FMT>& s1, int row0, int nrows, float* __restrict__ y) {
+                                        const SRow<FMT>& s1, int row0, int nrows, Y* __restrict__ y) {
   using C = Core<FMT, NB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t roff[C::kInstr];  // byte offset of each staged h row (relative to the tile's first row)
@@ -804,25 +805,30 @@ __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_
     const int r = 32 * b + l32;
     if (r >= nrows) continue;
     const float wr = sw[r];
-    float* yp = y + (int64_t)(row0 + r) * H + ncol + 4 * hh;
+    Y* yp = y + (int64_t)(row0 + r) * H + ncol + 4 * hh;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<float4*>(yp + 8 * q) =
-          make_float4(acc0[b][4 * q] * wr, acc0[b][4 * q + 1] * wr, acc0[b][4 * q + 2] * wr, acc0[b][4 * q + 3] * wr);
-      *reinterpret_cast<float4*>(yp + 32 + 8 * q) =
-          make_float4(acc1[b][4 * q] * wr, acc1[b][4 * q + 1] * wr, acc1[b][4 * q + 2] * wr, acc1[b][4 * q + 3] * wr);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f32x16& a = m ? acc1[b] : acc0[b];
+        const float v0 = a[4 * q] * wr, v1 = a[4 * q + 1] * wr, v2 = a[4 * q + 2] * wr, v3 = a[4 * q + 3] * wr;
+        if constexpr (sizeof(Y) == 4)
+          *reinterpret_cast<float4*>(yp + 32 * m + 8 * q) = make_float4(v0, v1, v2, v3);
+        else
+          *reinterpret_cast<uint2*>(yp + 32 * m + 8 * q) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      }
     }
   }
 }
 
-template <int FMT>
+template <int FMT, typename Y>
 __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict__ h, const float* __restrict__ wts,
                                                      int32_t E, int32_t H, int32_t I,
                                                      const uint8_t* __restrict__ wq, const float* __restrict__ ws,
                                                      const uint8_t* __restrict__ wsc,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
-                                                     const int32_t* __restrict__ perm_idx, float* __restrict__ y) {
+                                                     const int32_t* __restrict__ perm_idx, Y* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
   __shared__ float sw[kBM];
 
@@ -844,13 +850,13 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
   const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, H, r0, I, 0);
   const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, H, r1, I, 0);
   if (nrows > 192)
-    g2_tile<FMT, 8>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 8, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else if (nrows > 128)
-    g2_tile<FMT, 6>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 6, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else if (nrows > 64)
-    g2_tile<FMT, 4>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 4, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else
-    g2_tile<FMT, 2>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 2, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -1141,9 +1147,18 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* _
 }
 
 // ---------------------------------------------------------------------------
-// C1: out[t] = bf16(y[slot[t*K]] + y[slot[t*K+1]] + ... ) in k order.
+// C1: out[t] = bf16(y[slot[t*K]] + y[slot[t*K+1]] + ... ) in k order, the
+// sum in fp32 over fp32 or bf16 rows of y.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot,
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                     __uint_as_float(v.y & 0xffff0000u));
+}
+
+template <typename Y>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const Y* __restrict__ y, const int32_t* __restrict__ slot,
                                                           int32_t K, int32_t H, uint16_t* __restrict__ out) {
   const int64_t tok = blockIdx.x;
   const int32_t* sl = slot + tok * K;
@@ -1152,7 +1167,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
     for (int k = 0; k < K; ++k) {
       const int p = sl[k];
       if (p < 0) continue;
-      const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)p * H + 4 * n4);
+      const float4 v = load4(y + (int64_t)p * H + 4 * n4);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     *reinterpret_cast<uint2*>(out + tok * H + 4 * n4) =
@@ -1503,10 +1518,12 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
   g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, a.rb.offsets,
                                          a.rb.tile_start, a.rb.perm, a.h, nullptr);
   if (ev) (void)hipEventRecord(ev[2], s);
-  g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
-                                         a.rb.tile_start, a.rb.perm, a.y);
+  // y rows rounded to bf16 here (the fp32 workspace buffer holds them)
+  uint16_t* y16 = reinterpret_cast<uint16_t*>(a.y);
+  g2_kernel<FMT, uint16_t><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
+                                                   a.rb.tile_start, a.rb.perm, y16);
   if (ev) (void)hipEventRecord(ev[3], s);
-  combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.rb.slot, a.K, a.H, a.out);
+  combine_kernel<uint16_t><<<a.T, kThreads, 0, s>>>(y16, a.rb.slot, a.K, a.H, a.out);
   if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();
 }
@@ -1532,14 +1549,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   const RouteBuffers& r = a.rb;
   g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, r.offsets, r.tile_start,
                                          r.perm, a.h, a.gu_save);
-  g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets, r.tile_start,
-                                         r.perm, a.zdx);
+  g2_kernel<FMT, float><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
+                                                r.tile_start, r.perm, a.zdx);
   gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
   tgemm_kernel<FMT, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
                                                r.tile_start, r.perm, a.wts, a.gu_save, a.dgu);
   tgemm_kernel<FMT, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s, a.gu_c, r.offsets,
                                                r.tile_start, r.perm, nullptr, nullptr, a.zdx);
-  combine_kernel<<<a.T, kThreads, 0, s>>>(a.zdx, r.slot, a.K, a.H, a.grad_x);
+  combine_kernel<float><<<a.T, kThreads, 0, s>>>(a.zdx, r.slot, a.K, a.H, a.grad_x);
   return hipGetLastError();
 }
 

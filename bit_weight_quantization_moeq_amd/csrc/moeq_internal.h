@@ -103,7 +103,7 @@ struct ForwardArgs {
   uint16_t* out;            // [T][H]
   RouteBuffers rb;
   uint16_t* h;              // [T*K][I] bf16, expert-sorted rows
-  float* y;                 // [T*K][H] fp32, expert-sorted rows
+  float* y;                 // [T*K][H]: bf16 expert-sorted rows (tiled path) or fp32 (few-assignment path)
 };
 // events: NULL or 5 events recorded at the stage boundaries.
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);

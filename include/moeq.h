@@ -179,8 +179,9 @@ size_t moeq_experts_forward_workspace_bytes(int32_t T, int32_t K, const moeq_qwe
  *                 NF4 with double-quantized absmax, or int8)
  *   out_bf16      bf16 [T][H]:
  *                 out[t] = sum_k w[t,k] * down[e] @ (silu(gate[e] x_t) * up[e] x_t)
- *                 with the k terms added in order k = 0..K-1 (deterministic,
- *                 bit-identical run to run).
+ *                 with the k terms added in order k = 0..K-1 in fp32
+ *                 (deterministic, bit-identical run to run); above 512
+ *                 assignments each weighted term is first rounded to bf16.
  *   workspace     device memory of at least
  *                 moeq_experts_forward_workspace_bytes(T, K, gate_up, down).
  * Weights are dequantized tile by tile inside the kernels (bf16 operands,
