@@ -8,13 +8,13 @@
 // NF4 experts); its output is the (top_k_index, top_k_weights) pair of the
 // experts interface (unsloth-zoo issue #850, Suggested fix).
 //
-// One workgroup (4 waves) per 16 tokens.  Wave w computes the logits of the
-// expert blocks w, w + 4, ... (32 experts each) for the 16 tokens with
-// v_mfma_f32_32x32x16_bf16 (gate rows as A, token rows as B; token columns
-// 16..31 of the MFMA are zero), K running over H.  The logits meet in LDS;
-// then each wave takes 4 tokens: max, sum of exponentials and K rounds of
-// arg-max are wave reductions in a fixed butterfly order, so the result is
-// deterministic.
+// One workgroup (4 waves) per 16 tokens.  The waves split the expert blocks
+// (32 experts each) and, when there are few, H as well; each computes its
+// logits for the 16 tokens with v_mfma_f32_32x32x16_bf16 (gate rows as A,
+// token rows as B; token columns 16..31 of the MFMA are unused), K running
+// over H.  The logits meet in LDS; then each wave takes 4 tokens at once:
+// max, sum of exponentials and K rounds of arg-max are DPP wave reductions
+// in a fixed order, so the result is deterministic.
 #include "moeq_internal.h"
 
 namespace moeq {
@@ -29,9 +29,136 @@ constexpr int kTok = 16;  // tokens per workgroup
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// (value, index) order of the selection: larger value first, then lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Wave reductions on DPP lane moves (quad permutes, half-row and row
+// mirrors, then the row broadcasts that carry each row's result into the
+// next rows), read from lane 63: a fixed order, so deterministic, and short
+// dependent chains of VALU instructions.  `id` is the operation's identity,
+// returned by lanes a move does not write.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v, 0u));        // quad_perm [1,0,3,2]
+  v = max(v, dpp_u<0x4E>(v, 0u));        // quad_perm [2,3,0,1]
+  v = max(v, dpp_u<0x141>(v, 0u));       // row_half_mirror
+  v = max(v, dpp_u<0x140>(v, 0u));       // row_mirror: every lane holds its row's max
+  v = max(v, dpp_u<0x142, 0xA>(v, 0u));  // row_bcast15 into rows 1 and 3
+  v = max(v, dpp_u<0x143, 0xC>(v, 0u));  // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  const uint32_t id = 0xffffffffu;
+  v = min(v, dpp_u<0xB1>(v, id));
+  v = min(v, dpp_u<0x4E>(v, id));
+  v = min(v, dpp_u<0x141>(v, id));
+  v = min(v, dpp_u<0x140>(v, id));
+  v = min(v, dpp_u<0x142, 0xA>(v, id));
+  v = min(v, dpp_u<0x143, 0xC>(v, id));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_fsum(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_fsum(float v) {
+  v += dpp_fsum<0xB1>(v);
+  v += dpp_fsum<0x4E>(v);
+  v += dpp_fsum<0x141>(v);
+  v += dpp_fsum<0x140>(v);
+  v += dpp_fsum<0x142, 0xA>(v);
+  v += dpp_fsum<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// fp32 -> uint32 with the same order (-0 taken as +0 first); and back
+__device__ __forceinline__ uint32_t ord(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unord(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Softmax over the E logits of each of the block's tokens and the K rounds of
+// arg-max, from the logits in LDS; NPL logits per lane (E <= 64 NPL).
+template <int NPL>
+__device__ __forceinline__ void softmax_topk(const float* slog, int64_t t0, int32_t T, int32_t E, int32_t K,
+                                             int32_t renorm, int wave, int lane, int32_t* __restrict__ idx,
+                                             float* __restrict__ wts) {
+  // softmax and top-K: wave w takes tokens w, w + 4, w + 8, w + 12, all four
+  // at once (their cross-lane reductions are independent, so their shuffle
+  // latencies overlap)
+  constexpr int kTT = kTok / kWaves;                  // tokens per wave
+  float v[kTT][NPL];
+  float m[kTT], sum[kTT], inv[kTT];
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) {
+    const int tt = wave + kWaves * q;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      v[q][j] = (e < E) ? slog[tt * E + e] : -INFINITY;
+      lm = fmaxf(lm, v[q][j]);
+    }
+    m[q] = unord(wave_umax(ord(lm)));
+  }
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) ls += (lane + 64 * j < E) ? __expf(v[q][j] - m[q]) : 0.0f;
+    sum[q] = wave_fsum(ls);
+    inv[q] = 1.0f / sum[q];
+  }
+  // K rounds of arg-max: the largest logit first (wave max of its ordered
+  // bits), then the lowest index holding it (wave min), which its owner
+  // takes out of the race.  With renormalisation the sum of the selected
+  // probabilities comes from a first pass over the same selections, so the
+  // second pass can write the final weights.
+  float sel_sum[kTT];
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) sel_sum[q] = 1.0f;
+  for (int pass = renorm ? 0 : 1; pass < 2; ++pass) {
+    float u[kTT][NPL], acc_p[kTT];
+#pragma unroll
+    for (int q = 0; q < kTT; ++q) {
+      acc_p[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) u[q][j] = v[q][j];
+    }
+    for (int k = 0; k < K; ++k) {
+#pragma unroll
+      for (int q = 0; q < kTT; ++q) {
+        float lv = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) lv = fmaxf(lv, u[q][j]);
+        const uint32_t bm = wave_umax(ord(lv));
+        uint32_t li = 0xffffffffu;  // this lane's lowest index holding the maximum
+#pragma unroll
+        for (int j = NPL - 1; j >= 0; --j) {
+          const int e = lane + 64 * j;
+          if (e < E && ord(u[q][j]) == bm) li = (uint32_t)e;
+        }
+        const int bi = (int)wave_umin(li);
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+          if (lane + 64 * j == bi) u[q][j] = -INFINITY;
+        const float ex = __expf(unord(bm) - m[q]);
+        const int64_t tok = t0 + wave + kWaves * q;
+        if (pass == 0) {
+          acc_p[q] += ex * inv[q];
+        } else if (lane == 0 && tok < T) {
+          idx[tok * K + k] = bi;
+          wts[tok * K + k] = ex * (inv[q] / sel_sum[q]);
+        }
+      }
+    }
+    if (pass == 0) {
+#pragma unroll
+      for (int q = 0; q < kTT; ++q) sel_sum[q] = acc_p[q];
+    }
+  }
 }
 
 template <int RBW>  // expert blocks of 32 per wave
@@ -122,71 +249,16 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     __syncthreads();
   }
 
-  // softmax and top-K: wave w takes tokens w, w + 4, w + 8, w + 12
-  constexpr int kPer = (MOEQ_MAX_EXPERTS + 63) / 64;  // logits per lane (at most)
-  for (int tt = wave; tt < kTok; tt += kWaves) {
-    const int64_t tok = t0 + tt;
-    if (tok >= T) break;
-    float v[kPer];
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < E ? slog[tt * E + e] : -INFINITY;
-      m = fmaxf(m, v[j]);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) sum += (lane + 64 * j < E) ? __expf(v[j] - m) : 0.0f;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    const float inv = 1.0f / sum;
-    // K rounds of arg-max (every lane ends a round holding the winner, whose
-    // owner then takes it out of the race).  With renormalisation the sum of
-    // the selected probabilities comes from a first pass over the same
-    // selections, so the second pass can write the final weights.
-    float sel_sum = 1.0f;
-    for (int pass = renorm ? 0 : 1; pass < 2; ++pass) {
-      float u[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) u[j] = v[j];
-      float acc_p = 0.0f;
-      const float scale = inv / sel_sum;
-      for (int k = 0; k < K; ++k) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int e = lane + 64 * j;
-          if (e < E && better(u[j], e, bv, bi)) {
-            bv = u[j];
-            bi = e;
-          }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
-          const int oi = __shfl_xor(bi, o, 64);
-          if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-          if (lane + 64 * j == bi) u[j] = -INFINITY;
-        const float ex = __expf(bv - m);
-        if (pass == 0) {
-          acc_p += ex * inv;
-        } else if (lane == 0) {
-          idx[tok * K + k] = bi;
-          wts[tok * K + k] = ex * scale;
-        }
-      }
-      if (pass == 0) sel_sum = acc_p;
-    }
+  switch ((E + 63) / 64) {
+    case 1: softmax_topk<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 2: softmax_topk<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 3:
+    case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 5:
+    case 6:
+    case 7:
+    case 8: softmax_topk<8>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    default: softmax_topk<(MOEQ_MAX_EXPERTS + 63) / 64>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
   }
 }
 
