@@ -505,18 +505,27 @@ struct Core {
                                              int K, const uint8_t* q0, const SRow<FMT>& s0, const uint8_t* q1,
                                              const SRow<FMT>& s1, bool wave_on, f32x16 (&acc0)[NB],
                                              f32x16 (&acc1)[NB]) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    // wave-uniform, so each DMA's LDS base (M0) is scalar arithmetic rather
+    // than a vector result moved to a scalar register per instruction
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
     // source chunk of this lane within its row (the same for every instruction)
     const int chunk = (lane % kCpr) ^ swz(staged_row(wave, lane, 0));
-    char* stage0 = sX + staged_row(wave, 0, 0) * kCpr * 16;
+    // The DMA target is passed as a bare LDS address: with the array itself
+    // the compiler would make LDS reads wait for all DMAs in flight.  The
+    // explicit waits before each barrier order them instead.
+    uint32_t stage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(sX + staged_row(wave, 0, 0) * kCpr * 16);
+    asm volatile("" : "+s"(stage0));  // opaque, so it is not folded back into a pointer to the array
 
     // instruction i of the token DMA for K offset k0 into buffer buf
     auto stage_one = [&](int k0, int buf, int i) {
       int kk = k0 + 8 * chunk;
       kk = kk < K ? kk : 0;
-      __builtin_amdgcn_global_load_lds(tbase + roff[i] + 2 * kk,
-                                       stage0 + buf * buf_bytes + i * kWaves * kRpi * kCpr * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          tbase + roff[i] + 2 * kk,
+          (__attribute__((address_space(3))) void*)(size_t)(stage0 + buf * buf_bytes + i * kWaves * kRpi * kCpr * 16),
+          16, 0, 0);
     };
     auto stage = [&](int k0, int buf) {
 #pragma unroll
