@@ -19,7 +19,8 @@ same batch; ``router`` = the router front-end (gate GEMM, softmax, top-K)
 on the same batch; ``offload`` = the forward with the packed experts in
 pinned host memory and the next layer prefetched; ``double_quant`` = the
 same quantize, forward, decode and backward with double-quantized absmax;
-``codec`` = row-wise int8 quantize and the two dequantizes;
+``codec`` = row-wise int8 quantize and the two dequantizes; ``load`` = the
+quantize-on-load pass over 16 OLMoE-shaped and 48 Qwen3-shaped layers;
 ``cpu_baseline`` = the CPU oracle on a bounded sample of the same workload.
 Inputs are seeded synthetic tensors resident in HBM before the timed region.
 """
@@ -58,6 +59,7 @@ def parse():
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-offload", action="store_true")
     ap.add_argument("--no-double-quant", action="store_true")
+    ap.add_argument("--no-load", action="store_true")
     return ap.parse_args()
 
 
@@ -341,6 +343,38 @@ def double_quant_figures(torch, np, moeq, syn, s, gu, dn, x, idx, wts, dev, copy
                             "bits_per_weight_double_quant": 8.0 * (qg.nbytes() + qd.nbytes()) / nel}}
 
 
+def load_figures(torch, np, moeq, syn, dev, copy_GBps):
+    """Quantize-on-load of whole models' expert stacks: the OLMoE shape's 16
+    layers and the Qwen3 shape's 48 layers, NF4.  One layer's bf16 weights
+    are generated once and quantized `layers` times back-to-back (every layer
+    streams the same bytes from HBM; a layer's 1.2 GB outgrows every cache),
+    with events around the whole pass."""
+    out = {}
+    for name, layers in (("olmoe", 16), ("qwen3", 48)):
+        s = syn.SHAPES[name]
+        gu = syn.expert_weights(s.gate_up_shape, tensor=syn.GATE_UP, device=dev)
+        dn = syn.expert_weights(s.down_shape, tensor=syn.DOWN, device=dev)
+        qg = moeq.QWeight.empty(moeq.FMT_NF4, *s.gate_up_shape, device=dev)
+        qd = moeq.QWeight.empty(moeq.FMT_NF4, *s.down_shape, device=dev)
+        moeq.moeq_quantize_nf4(gu, out=qg)
+        moeq.moeq_quantize_nf4(dn, out=qd)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(layers):
+            moeq.moeq_quantize_nf4(gu, out=qg)
+            moeq.moeq_quantize_nf4(dn, out=qd)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        nel = layers * (gu.numel() + dn.numel())
+        out[name] = {"layers": layers, "ms": ms, "bf16_GB": nel * 2 / 1e9,
+                     "packed_GB": layers * (qg.nbytes() + qd.nbytes()) / 1e9,
+                     "GBps": nel * NF4_BYTES_PER_ELEM / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nel * NF4_BYTES_PER_ELEM / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del gu, dn, qg, qd
+    return out
+
+
 def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
     """Row-wise int8 quantize on the gpt-oss-shaped experts and dequantize of
     both formats: algorithmic bytes / event time."""
@@ -529,6 +563,8 @@ def main():
         result["double_quant"] = double_quant_figures(torch, np, moeq, syn, s, gu, dn, x, idx, wts, dev, copy_GBps)
     if not args.no_codec:
         result["codec"] = codec_figures(torch, np, moeq, syn, dev, copy_GBps)
+    if not args.no_load:
+        result["load"] = load_figures(torch, np, moeq, syn, dev, copy_GBps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, gu, dn, x, idx, wts, T)

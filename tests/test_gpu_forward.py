@@ -66,7 +66,7 @@ CASES = [
     ("olmoe", 1, 1, None), ("olmoe", 32, 3, None), ("olmoe", 4096, 2, 512),
     ("qwen3", 1, 1, None), ("qwen3", 64, 2, None), ("qwen3", 8192, 2, 512),
     ("gptoss", 16, 3, None), ("gptoss", 2048, 2, 720),
-    ("mixtral", 1, 1, 256), ("mixtral", 512, 1, 256),
+    ("mixtral", 1, 1, 256), ("mixtral", 512, 1, 256), ("mixtral", 16384, 1, 256),
 ]
 
 
