@@ -293,13 +293,17 @@ __device__ __forceinline__ bf16x8 i8_frag(uint32_t w0, uint32_t w1, float s, flo
 template <int FMT>
 struct RowCodes {
   uint4 c0, c1;
-  Scale<FMT> scale;
+  Scale<FMT> scale;  // as loaded; sc() is the one to use
+  uint32_t m;        // all ones when the step is in range, else zero
 
-  // Exactly kLoads vector loads per call (the K-step pipeline counts on it):
-  // row_base: codes of the row (always a valid row); srow: scales of the
-  // row; k0: K step start; hh: lane half; K: row length; ok: the row is
-  // real.  Outside the row or the K range the loads read the row start and
-  // the result is replaced by zeros.
+  // Exactly kLoads vector loads per call (the K-step pipeline counts on it),
+  // always issued, with no branch around them, so that a caller can place
+  // them between MFMAs: row_base: codes of the row (always a valid row);
+  // srow: scales of the row; k0: K step start; hh: lane half; K: row length;
+  // ok: the row is real.  Outside the row or the K range the loads read the
+  // row start and the step is zeroed through its scale when consumed (NF4:
+  // zero absmax -> all-zero table; int8: zero scale -> the A operand is
+  // exactly zero), so nothing waits on the loads here.
   static constexpr int kLoads = 2 + SRow<FMT>::kLoads;
   __device__ __forceinline__ void fetch(const uint8_t* row_base, const SRow<FMT>& srow, int k0, int hh, int K,
                                         bool ok) {
@@ -308,13 +312,13 @@ struct RowCodes {
     const bool in = ok && kk < K;
     const int kc = in ? kk : 0;
     const uint4* p = reinterpret_cast<const uint4*>(row_base + (kNf4Codes<FMT> ? kc / 2 : kc));
-    const uint4 a = p[0], b = p[1];
-    const Scale<FMT> sc = srow.load(kNf4Codes<FMT> ? kc / kNf4Block : 0);
-    // NF4: zero absmax -> all-zero table; int8: zero scale -> the A operand is exactly zero
-    c0 = in ? a : make_uint4(0, 0, 0, 0);
-    c1 = in ? b : make_uint4(0, 0, 0, 0);
-    scale = sc.or_zero(in);
+    c0 = p[0];
+    c1 = p[1];
+    scale = srow.load(kNf4Codes<FMT> ? kc / kNf4Block : 0);
+    m = in ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));  // opaque, so the select is not folded into a branch around the loads
   }
+  __device__ __forceinline__ Scale<FMT> sc() const { return scale.masked(m); }
   __device__ __forceinline__ uint32_t word(int i) const {
     const uint4& c = (i < 4) ? c0 : c1;
     const int j = i & 3;
@@ -353,7 +357,7 @@ struct StreamCodes {
   }
   __device__ __forceinline__ RowCodes<FMT> use() const {
     RowCodes<FMT> r = raw;
-    r.scale = raw.scale.masked(m);
+    r.m = m;
     return r;
   }
 };
@@ -361,11 +365,11 @@ struct StreamCodes {
 template <int FMT>
 struct Dequant {  // NF4, plain or with double-quantized absmax
   Nf4Table t;
-  __device__ __forceinline__ void prepare(const RowCodes<FMT>& r) { t = nf4_table(r.scale.value()); }
+  __device__ __forceinline__ void prepare(const RowCodes<FMT>& r) { t = nf4_table(r.sc().value()); }
   // the same table in kPrepStages pieces: piece q holds levels 4q .. 4q+3
   static constexpr int kPrepStages = 4;
   __device__ __forceinline__ void prep_stage(int q, const RowCodes<FMT>& r) {
-    float a = r.scale.value();
+    float a = r.sc().value();
     pin_in(a);
     const uint32_t p0 = pack_bf16x2(__uint_as_float(kNf4LevelBits[4 * q]) * a,
                                     __uint_as_float(kNf4LevelBits[4 * q + 1]) * a);
@@ -394,7 +398,7 @@ template <>
 struct Dequant<MOEQ_FMT_INT8_ROWWISE> {
   float s, ns128;
   __device__ __forceinline__ void prepare(const RowCodes<MOEQ_FMT_INT8_ROWWISE>& r) {
-    s = r.scale.value();
+    s = r.sc().value();
     ns128 = -128.0f * s;
   }
   static constexpr int kPrepStages = 1;
@@ -563,7 +567,10 @@ struct Core {
     // prefetches a harmless extra step (zero codes, an in-range row).
     constexpr int kS = kStep / 16;         // MFMA steps per K step
     constexpr int kSlots = 2 * NB;         // MFMAs per MFMA step
-    constexpr int kDmaSub = kS / 2;        // MFMA steps that carry the DMAs
+    constexpr int kDma0 = 0;                      // first MFMA step that carries token DMAs
+    constexpr int kDmaSub = kS - 1;               // MFMA steps that carry them
+    constexpr int kFetch0 = kS > 4 ? 1 : 0;       // MFMA steps that load the next step's codes
+    constexpr int kFetch1 = kS > 4 ? 3 : 1;
     constexpr int kFragWork = 2 * FragStages<FMT>::kStages;
     constexpr int kPrepWork = 2 * Dequant<FMT>::kPrepStages;
     constexpr int kLastWork = kPrepWork + kFragWork;
@@ -575,9 +582,6 @@ struct Core {
         const int slot = ((kCpr / 2) * hh + s_) ^ rsw;
         return *reinterpret_cast<const bf16x8*>(xb + (32 * b * kCpr + slot) * 16);
       };
-      nxt.c0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
-      nxt.c1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
-      __builtin_amdgcn_sched_barrier(0);  // the DMAs below must issue after the code loads
       bf16x8 a0 = cur.a0, a1 = cur.a1;
       bf16x8 xf[NB];
 #pragma unroll
@@ -590,12 +594,14 @@ struct Core {
           f0.begin(cur.c0, s + 1);
           f1.begin(cur.c1, s + 1);
         }
-        if (s < kDmaSub) {
+        if (s >= kDma0 && s < kDma0 + kDmaSub) {
 #pragma unroll
-          for (int i = s * kInstr / kDmaSub; i < (s + 1) * kInstr / kDmaSub; ++i)
+          for (int i = (s - kDma0) * kInstr / kDmaSub; i < (s - kDma0 + 1) * kInstr / kDmaSub; ++i)
             stage_one(dstep * kStep, dstep % kNbuf, i);
-          __builtin_amdgcn_sched_barrier(0);
         }
+        if (s == kFetch0) nxt.c0.fetch(q0, s0, (ks + 1) * kStep, hh, K, wave_on);
+        if (s == kFetch1) nxt.c1.fetch(q1, s1, (ks + 1) * kStep, hh, K, wave_on);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
           const int b = i >> 1;
