@@ -177,6 +177,18 @@ __device__ __forceinline__ void pin_in(uint32_t& x) { asm volatile("" : "+v"(x))
 __device__ __forceinline__ void pin_in(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin_out(uint32_t x) { asm volatile("" ::"v"(x)); }
 
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4 with the LDS base in M0).  Written as inline
+// assembly so that the compiler does not see an LDS write it cannot order:
+// with the builtin it waits for every LDS access in flight (lgkmcnt(0)) at
+// each later LDS use, which would also wait for fragment reads issued ahead
+// of time.  The caller orders the copy with explicit vmcnt waits before a
+// barrier.  The DMA reads M0 one wait state after it is written.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(bf16x8, v);
@@ -1287,22 +1299,65 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     asm volatile("" : "+v"(m));  // opaque: keeps the select from becoming a branch around the loads
     c.m = m;
   };
-  auto wstore = [&](const WCodes& c, int buf) {
+  // The dequantization of one step's W row quarter into LDS, cut into work
+  // items of a few VALU instructions each so that a K step can slot one item
+  // after each MFMA (the same arithmetic and bits as moeq_dequantize):
+  //   NF4:  4 table stages, then per 8-column fragment f: 4 stages and its store;
+  //   int8: the scale pair, then per fragment f: 2 stages and its store.
+  struct WStage {
+    float sc;
+    Nf4Table tb;
+    Nf4FragStages f4;
+    FragStages<MOEQ_FMT_INT8_ROWWISE> f8;
+    Dequant<MOEQ_FMT_INT8_ROWWISE> d8;
+  };
+  constexpr int kWItems = kNf4Codes<FMT> ? 4 + 4 * 5 : 1 + 4 * 3;
+  auto witem = [&](int j, const WCodes& c, WStage& w, int buf) {
     char* dst = sW(buf) + wr * kTpitch + 64 * (t & 3);
-    const float sc = c.s.masked(c.m).value();
     if constexpr (kNf4Codes<FMT>) {
-      const Nf4Table tb = nf4_table(sc);
-      *reinterpret_cast<bf16x8*>(dst) = nf4_frag(tb, c.a.x);
-      *reinterpret_cast<bf16x8*>(dst + 16) = nf4_frag(tb, c.a.y);
-      *reinterpret_cast<bf16x8*>(dst + 32) = nf4_frag(tb, c.a.z);
-      *reinterpret_cast<bf16x8*>(dst + 48) = nf4_frag(tb, c.a.w);
+      if (j < 4) {
+        if (j == 0) w.sc = c.s.masked(c.m).value();
+        float a = w.sc;
+        pin_in(a);
+        const uint32_t p0 = pack_bf16x2(__uint_as_float(kNf4LevelBits[4 * j]) * a,
+                                        __uint_as_float(kNf4LevelBits[4 * j + 1]) * a);
+        const uint32_t p1 = pack_bf16x2(__uint_as_float(kNf4LevelBits[4 * j + 2]) * a,
+                                        __uint_as_float(kNf4LevelBits[4 * j + 3]) * a);
+        w.tb.lo[j] = perm(p1, p0, 0x06040200u);
+        w.tb.hi[j] = perm(p1, p0, 0x07050301u);
+        pin_out(w.tb.lo[j]), pin_out(w.tb.hi[j]);
+      } else {
+        const int f = (j - 4) / 5, k = (j - 4) % 5;
+        if (k < 4) {
+          if (k == 0) w.f4.w = f == 0 ? c.a.x : (f == 1 ? c.a.y : (f == 2 ? c.a.z : c.a.w));
+          w.f4.stage(k, w.tb);
+        } else {
+          *reinterpret_cast<bf16x8*>(dst + 16 * f) = w.f4.value();
+        }
+      }
     } else {
-      const float ns = -128.0f * sc;
-      *reinterpret_cast<bf16x8*>(dst) = i8_frag(c.a.x, c.a.y, sc, ns);
-      *reinterpret_cast<bf16x8*>(dst + 16) = i8_frag(c.a.z, c.a.w, sc, ns);
-      *reinterpret_cast<bf16x8*>(dst + 32) = i8_frag(c.b.x, c.b.y, sc, ns);
-      *reinterpret_cast<bf16x8*>(dst + 48) = i8_frag(c.b.z, c.b.w, sc, ns);
+      if (j == 0) {
+        w.d8.s = c.s.masked(c.m).value();
+        w.d8.ns128 = -128.0f * w.d8.s;
+      } else {
+        const int f = (j - 1) / 3, k = (j - 1) % 3;
+        if (k < 2) {
+          if (k == 0) {
+            const uint4& q = f < 2 ? c.a : c.b;
+            w.f8.w[0] = (f & 1) ? q.z : q.x;
+            w.f8.w[1] = (f & 1) ? q.w : q.y;
+          }
+          w.f8.stage(k, w.d8);
+        } else {
+          *reinterpret_cast<bf16x8*>(dst + 16 * f) = w.f8.value();
+        }
+      }
     }
+  };
+  auto wstore = [&](const WCodes& c, int buf) {
+    WStage w;
+#pragma unroll
+    for (int j = 0; j < kWItems; ++j) witem(j, c, w, buf);
   };
 
   // token tile loader: instruction i of wave w stages rows 8 (4 i + w) .. +7,
@@ -1322,14 +1377,14 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
   // The explicit waits before each barrier order them instead.
   uint32_t vlds = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)sV(0);
   asm volatile("" : "+s"(vlds));  // opaque, so it is not folded back into a pointer to the array
-  auto vstage = [&](int ks, int buf) {
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the LDS target (M0) is scalar
+  auto vstage_one = [&](int ks, int buf, int i) {
     const int kk = (ks < nks ? ks * kTk : 0) + 8 * vchunk;
+    lds_dma16(vbase + voff[i] + 2 * kk, vlds + buf * kVBytes + (8 * (4 * i + wave_u)) * 128);
+  };
+  auto vstage = [&](int ks, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(vbase + voff[i] + 2 * kk,
-                                       (__attribute__((address_space(3))) void*)(size_t)(vlds + buf * kVBytes +
-                                                                                         (8 * (4 * i + wave)) * 128),
-                                       16, 0, 0);
+    for (int i = 0; i < 8; ++i) vstage_one(ks, buf, i);
   };
 
   // A operand addresses (ds_read_b64_tr_b16): lane L = lane % 16 of group
@@ -1346,34 +1401,19 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[m][b] = (f32x16){};
 
-  auto mfma_step = [&](int buf) {
-#pragma unroll
-    for (int s4 = 0; s4 < kTk / 16; ++s4) {
-      bf16x8 af[2], bf[4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const char* base = sW(buf) + (16 * s4) * kTpitch + 2 * (cw + 32 * m) + a_off;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 4 * kTpitch));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        af[m] = as_bf16x8(l2.x, l2.y, h2.x, h2.y);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int row = tw + 32 * b + l32;
-        const int slot = (2 * s4 + hh) ^ (row & 7);
-        bf[b] = *reinterpret_cast<const bf16x8*>(sV(buf) + row * 128 + slot * 16);
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[m][b] = mfma(af[m], bf[b], acc[m][b]);
-    }
-  };
-
-  // Step ks: stage step ks+1 (token DMA, W dequant from codes loaded a step
-  // ago), load step ks+2's codes, multiply step ks, then wait for this
-  // thread's DMA and meet at the barrier.  Two code register sets in turn.
+  // Step ks: multiply step ks from buffer buf while staging step ks + 1 into
+  // buffer buf ^ 1 (read last in step ks - 1, before the barrier that ended
+  // it): after each of the 32 MFMAs one dequantization work item of the codes
+  // loaded a step ago, one token DMA after each even MFMA of the first 16,
+  // then the loads of step ks + 2's codes.  The code loads are the last loads
+  // of the step, so the wait before the barrier can leave exactly them in
+  // flight (every older load, the DMAs included, has landed).  The fragments
+  // of each 16-row sub-step are read from LDS one sub-step ahead.  Two code
+  // register sets in turn.
+  constexpr int kSub = kTk / 16;          // MFMA sub-steps per step
+  constexpr int kWSlots = kSub * 8;       // MFMAs per step (2 column blocks x 4 token blocks each)
+  constexpr int kFetchSlot = 16;          // MFMA after which the next codes load
+  static_assert(kWItems <= kWSlots && 2 * 7 < kFetchSlot, "step schedule");
   WCodes ca, cb;
   wfetch(ca, 0);
   vstage(0, 0);
@@ -1381,25 +1421,43 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
   wfetch(ca, 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // (the buffer index is a compile-time constant in each copy, so the
-  // compiler can tell the DMA's LDS target from the buffer being read)
+  auto frags = [&](int buf, int s4, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const char* base = sW(buf) + (16 * s4) * kTpitch + 2 * (cw + 32 * m) + a_off;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 4 * kTpitch));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      af[m] = as_bf16x8(l2.x, l2.y, h2.x, h2.y);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = tw + 32 * b + l32;
+      const int slot = (2 * s4 + hh) ^ (row & 7);
+      bf[b] = *reinterpret_cast<const bf16x8*>(sV(buf) + row * 128 + slot * 16);
+    }
+  };
   auto kstep = [&](auto bufc, int ks, WCodes& cn, WCodes& cnn) {
     constexpr int buf = decltype(bufc)::value;
-    __builtin_amdgcn_sched_barrier(0);  // nothing of the next step moves up here (it would wait for its codes)
-    // dequantize step ks + 1's codes (loaded a step ago) before issuing the
-    // DMA, so waiting for the codes does not also wait for the DMA
-    wstore(cn, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    vstage(ks + 1, buf ^ 1);
-    // The code loads must issue after the DMAs: the wait before the barrier
-    // counts on the DMAs being the older loads.
-    __builtin_amdgcn_sched_barrier(0);
-    wfetch(cnn, ks + 2);
-    mfma_step(buf);
-    // The codes just fetched may stay in flight; every earlier load (the
-    // DMA for step ks + 1) has landed, and this wave's LDS writes are done.
-    // A release fence would also wait for the codes (LDS DMA counts as a
-    // vector load), so the barrier is bare, with an acquire fence after it.
+    WStage w;
+    bf16x8 af[2][2], bf[2][4];
+    frags(buf, 0, af[0], bf[0]);
+#pragma unroll
+    for (int s4 = 0; s4 < kSub; ++s4) {
+      const int cur = s4 & 1;
+      if (s4 + 1 < kSub) frags(buf, s4 + 1, af[cur ^ 1], bf[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = i >> 2, b = i & 3, slot = 8 * s4 + i;
+        acc[m][b] = mfma(af[cur][m], bf[cur][b], acc[m][b]);
+        if (slot < kWItems) witem(slot, cn, w, buf ^ 1);
+        if ((slot & 1) == 0 && slot / 2 < 8) vstage_one(ks + 1, buf ^ 1, slot / 2);
+        if (slot == kFetchSlot) wfetch(cnn, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWLoads>);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
