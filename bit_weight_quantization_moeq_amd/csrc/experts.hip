@@ -705,7 +705,27 @@ struct Lds {
   // bytes per buffer (largest tile), and the LDS all paths fit in
   static constexpr int kBuf = Core<FMT, kBM / 32>::kBufBytes;
   static constexpr int kTotal = 2 * kBuf > 3 * Core<FMT, 6>::kBufBytes ? 2 * kBuf : 3 * Core<FMT, 6>::kBufBytes;
+  // G2 also stages its bf16 output tile (kBM rows, padded) in the same array
+  static constexpr int kYTile = kBM * (2 * kG2Rows + 16);
+  static constexpr int kG2 = kTotal > kYTile ? kTotal : kYTile;
 };
+
+// Copies a staged bf16 tile out of LDS, whole rows at a time (G2's output:
+// measured, G1's narrower h tile gains nothing from it): row r (r <
+// nrows <= kBM) of kChunks 16-B chunks at src + r * kPitch goes to
+// dst + r * ld, chunks whose first element is at or past `cols` skipped (cols
+// is a multiple of 8).  A fixed, unrolled trip count, so the LDS reads are
+// issued ahead of the stores.
+template <int kChunks, int kPitch>
+__device__ __forceinline__ void copy_rows(const char* src, int nrows, int cols, uint16_t* __restrict__ dst, int64_t ld) {
+  const int total = nrows * kChunks;
+#pragma unroll
+  for (int u = 0; u < kBM * kChunks / kThreads; ++u) {
+    const int c = threadIdx.x + u * kThreads, r = c / kChunks, k = c % kChunks;
+    if (c < total && 8 * k < cols)
+      *reinterpret_cast<uint4*>(dst + r * ld + 8 * k) = *reinterpret_cast<const uint4*>(src + r * kPitch + 16 * k);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // G1: h[p][j] = bf16(silu(gate_j . x) * (up_j . x)) for the tile's rows p.
@@ -825,8 +845,36 @@ __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_
   }
   C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(h + (int64_t)row0 * I), roff, I, q0, s0, q1, s1, on,
          acc0, acc1);
-  if (!on) return;
   const int l32 = lane & 31, hh = lane >> 5;
+  if constexpr (sizeof(Y) == 2) {
+    // bf16 y through LDS, so that global stores write whole rows (a direct
+    // store from the MFMA layout touches 32 rows per instruction)
+    constexpr int kPitch = 2 * kG2Rows + 16;  // bytes per staged row (16-B aligned, 8-B writes 2-way at most)
+    static_assert(32 * NB * kPitch <= Lds<FMT>::kG2, "y tile fits the LDS array");
+    __builtin_amdgcn_s_waitcnt(0);  // token DMAs of the extra prefetched step may still be landing
+    __syncthreads();
+    if (on) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float wr = sw[32 * b + l32];
+        char* rowp = sX + (32 * b + l32) * kPitch + 2 * (64 * wave + 4 * hh);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const f32x16& a = m ? acc1[b] : acc0[b];
+            *reinterpret_cast<uint2*>(rowp + 2 * (32 * m + 8 * q)) =
+                make_uint2(pack_bf16x2(a[4 * q] * wr, a[4 * q + 1] * wr), pack_bf16x2(a[4 * q + 2] * wr, a[4 * q + 3] * wr));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int n0 = ncol - 64 * wave;
+    copy_rows<2 * kG2Rows / 16, kPitch>(sX, nrows, H - n0, reinterpret_cast<uint16_t*>(y) + (int64_t)row0 * H + n0, H);
+    return;
+  }
+  if (!on) return;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int r = 32 * b + l32;
@@ -856,7 +904,7 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx, Y* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
+  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kG2];
   __shared__ float sw[kBM];
 
   int e, mt, ct;
