@@ -705,25 +705,27 @@ struct Lds {
   // bytes per buffer (largest tile), and the LDS all paths fit in
   static constexpr int kBuf = Core<FMT, kBM / 32>::kBufBytes;
   static constexpr int kTotal = 2 * kBuf > 3 * Core<FMT, 6>::kBufBytes ? 2 * kBuf : 3 * Core<FMT, 6>::kBufBytes;
-  // G2 also stages its bf16 output tile (kBM rows, padded) in the same array
+  // G1 and G2 also stage output tiles (kBM rows of 512 B, padded) in the same array
   static constexpr int kYTile = kBM * (2 * kG2Rows + 16);
   static constexpr int kG2 = kTotal > kYTile ? kTotal : kYTile;
 };
 
-// Copies a staged bf16 tile out of LDS, whole rows at a time (G2's output:
-// measured, G1's narrower h tile gains nothing from it): row r (r <
-// nrows <= kBM) of kChunks 16-B chunks at src + r * kPitch goes to
-// dst + r * ld, chunks whose first element is at or past `cols` skipped (cols
-// is a multiple of 8).  A fixed, unrolled trip count, so the LDS reads are
-// issued ahead of the stores.
-template <int kChunks, int kPitch>
-__device__ __forceinline__ void copy_rows(const char* src, int nrows, int cols, uint16_t* __restrict__ dst, int64_t ld) {
+// Copies a tile staged in LDS out to global memory, whole rows at a time:
+// row r (r < nrows <= kRows) of kChunks 16-B chunks at src + r * kPitch goes
+// to dst + r * ld (elements of T), chunks whose first element is at or past
+// `cols` skipped (cols a multiple of 16 / sizeof(T)).  A fixed, unrolled trip
+// count, so the LDS reads are issued ahead of the stores.  Stored straight
+// from the MFMA accumulator layout, each store instruction would touch 32
+// rows (32 cache lines, a 16-B piece of each).
+template <typename T, int kRows, int kChunks, int kPitch>
+__device__ __forceinline__ void copy_rows(const char* src, int nrows, int cols, T* __restrict__ dst, int64_t ld) {
+  constexpr int kPer = 16 / (int)sizeof(T);  // elements per chunk
   const int total = nrows * kChunks;
 #pragma unroll
-  for (int u = 0; u < kBM * kChunks / kThreads; ++u) {
+  for (int u = 0; u < kRows * kChunks / kThreads; ++u) {
     const int c = threadIdx.x + u * kThreads, r = c / kChunks, k = c % kChunks;
-    if (c < total && 8 * k < cols)
-      *reinterpret_cast<uint4*>(dst + r * ld + 8 * k) = *reinterpret_cast<const uint4*>(src + r * kPitch + 16 * k);
+    if (c < total && kPer * k < cols)
+      *reinterpret_cast<uint4*>(dst + r * ld + kPer * k) = *reinterpret_cast<const uint4*>(src + r * kPitch + 16 * k);
   }
 }
 
@@ -751,34 +753,52 @@ __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32
     accU[b] = (f32x16){};
   }
   C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(x), roff, H, gq, gs, uq, us, wave_on, accG, accU);
-  if (!wave_on) return;
   // lane holds, per token block b and register quad q, the four h columns
   // jcol + 8q + 4*hh + 0..3 of token row 32b + l32.
   const int l32 = lane & 31, hh = lane >> 5;
+  if (wave_on) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int r = 32 * b + l32;
-    if (r >= nrows) continue;
-    uint16_t* hp = h + (int64_t)(row0 + r) * I + jcol + 4 * hh;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = accG[b][4 * q + i], u = accU[b][4 * q + i];
-        v[i] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-      }
-      *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    }
-    if (gu_save) {  // the backward keeps g and u of every sorted row: [n][2I] fp32
-      float* gp = gu_save + (int64_t)(row0 + r) * 2 * I + jcol + 4 * hh;
+    for (int b = 0; b < NB; ++b) {
+      const int r = 32 * b + l32;
+      if (r >= nrows) continue;
+      uint16_t* hp = h + (int64_t)(row0 + r) * I + jcol + 4 * hh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<float4*>(gp + 8 * q) =
-            make_float4(accG[b][4 * q], accG[b][4 * q + 1], accG[b][4 * q + 2], accG[b][4 * q + 3]);
-        *reinterpret_cast<float4*>(gp + I + 8 * q) =
-            make_float4(accU[b][4 * q], accU[b][4 * q + 1], accU[b][4 * q + 2], accU[b][4 * q + 3]);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = accG[b][4 * q + i], u = accU[b][4 * q + i];
+          v[i] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+        }
+        *reinterpret_cast<uint2*>(hp + 8 * q) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
+    }
+  }
+  if (gu_save) {
+    // The backward keeps g and u of every sorted row ([n][2I] fp32), staged
+    // through LDS (the token buffers, free once the last DMAs have landed) so
+    // that the global stores write whole rows: first g, then u.  Every wave
+    // takes part in the barriers.
+    constexpr int kPitch = 4 * kG1Cols + 16;
+    static_assert(32 * NB * kPitch <= Lds<FMT>::kG2, "g tile fits the LDS array");
+    const int j0 = jcol - 32 * wave;
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      __syncthreads();
+      if (wave_on) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const f32x16& a = part ? accU[b] : accG[b];
+          char* rowp = sX + (32 * b + l32) * kPitch + 4 * (32 * wave + 4 * hh);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(rowp + 4 * 8 * q) = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+      }
+      __syncthreads();
+      copy_rows<float, kBM, 4 * kG1Cols / 16, kPitch>(sX, nrows, I - j0, gu_save + (int64_t)row0 * 2 * I + part * I + j0,
+                                                      2 * I);
     }
   }
 }
@@ -791,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ tile_start,
                                                      const int32_t* __restrict__ perm_idx,
                                                      uint16_t* __restrict__ h, float* __restrict__ gu_save) {
-  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kTotal];
+  __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kG2];
 
   int e, mt, ct;
   if (!decode_work(tile_start, E, (I + kG1Cols - 1) / kG1Cols, e, mt, ct)) return;
@@ -871,27 +891,39 @@ __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_
     }
     __syncthreads();
     const int n0 = ncol - 64 * wave;
-    copy_rows<2 * kG2Rows / 16, kPitch>(sX, nrows, H - n0, reinterpret_cast<uint16_t*>(y) + (int64_t)row0 * H + n0, H);
+    copy_rows<uint16_t, kBM, 2 * kG2Rows / 16, kPitch>(sX, nrows, H - n0,
+                                                      reinterpret_cast<uint16_t*>(y) + (int64_t)row0 * H + n0, H);
     return;
-  }
-  if (!on) return;
+  } else {
+    // fp32 y (the backward's unweighted z) the same way, 128 rows per round
+    constexpr int kPitch = 4 * kG2Rows + 16;
+    constexpr int kRound = 4;  // token blocks per round
+    static_assert(32 * kRound * kPitch <= Lds<FMT>::kG2, "y rows fit the LDS array");
+    const int n0 = ncol - 64 * wave;
+    __builtin_amdgcn_s_waitcnt(0);  // token DMAs of the extra prefetched step may still be landing
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int r = 32 * b + l32;
-    if (r >= nrows) continue;
-    const float wr = sw[r];
-    Y* yp = y + (int64_t)(row0 + r) * H + ncol + 4 * hh;
+    for (int b0 = 0; b0 < NB; b0 += kRound) {
+      __syncthreads();  // the LDS is free (token buffers, or the previous round's rows)
+      if (on) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+        for (int b = b0; b < (b0 + kRound < NB ? b0 + kRound : NB); ++b) {
+          const float wr = sw[32 * b + l32];
+          char* rowp = sX + (32 * (b - b0) + l32) * kPitch + 4 * (64 * wave + 4 * hh);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const f32x16& a = m ? acc1[b] : acc0[b];
-        const float v0 = a[4 * q] * wr, v1 = a[4 * q + 1] * wr, v2 = a[4 * q + 2] * wr, v3 = a[4 * q + 3] * wr;
-        if constexpr (sizeof(Y) == 4)
-          *reinterpret_cast<float4*>(yp + 32 * m + 8 * q) = make_float4(v0, v1, v2, v3);
-        else
-          *reinterpret_cast<uint2*>(yp + 32 * m + 8 * q) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const f32x16& a = m ? acc1[b] : acc0[b];
+              *reinterpret_cast<float4*>(rowp + 4 * (32 * m + 8 * q)) =
+                  make_float4(a[4 * q] * wr, a[4 * q + 1] * wr, a[4 * q + 2] * wr, a[4 * q + 3] * wr);
+            }
+          }
+        }
       }
+      __syncthreads();
+      const int rows = nrows - 32 * b0;
+      copy_rows<float, 32 * kRound, 4 * kG2Rows / 16, kPitch>(sX, rows < 32 * kRound ? rows : 32 * kRound, H - n0,
+                                                              reinterpret_cast<float*>(y) + (int64_t)(row0 + 32 * b0) * H + n0, H);
     }
   }
 }
