@@ -1333,7 +1333,10 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
                                                         const float* __restrict__ gu_save, void* __restrict__ out) {
   // one LDS array: the dequantized W tiles, then the token tiles
   constexpr int kWBytes = kTk * kTpitch, kVBytes = kBM * kTk * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kWBytes + 2 * kVBytes];
+  // (T2 also stages its fp32 output tile here: kBM rows of kTcols floats, padded)
+  constexpr int kOutPitch = 4 * kTcols + 16;
+  constexpr int kSmem = 2 * kWBytes + 2 * kVBytes > kBM * kOutPitch ? 2 * kWBytes + 2 * kVBytes : kBM * kOutPitch;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ float sw[kBM];
   auto sW = [&](int b) { return smem + b * kWBytes; };
   auto sV = [&](int b) { return smem + 2 * kWBytes + b * kVBytes; };
@@ -1551,6 +1554,25 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
 
   // epilogue: lane holds, per column block m and token block b, output
   // columns cw + 32 m + 8 q + 4 hh + 0..3 of tile row tw + 32 b + l32
+  if constexpr (MODE == 2) {
+    // dx through LDS, so that the global stores write whole rows
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[m][b];
+          *reinterpret_cast<float4*>(smem + (tw + 32 * b + l32) * kOutPitch + 4 * (cw + 32 * m + 8 * q + 4 * hh)) =
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+    __syncthreads();
+    copy_rows<float, kBM, 4 * kTcols / 16, kOutPitch>(smem, nrows, C - c0, static_cast<float*>(out) + (int64_t)row0 * C + c0,
+                                                      C);
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int r = tw + 32 * b + l32;
