@@ -5,10 +5,12 @@ Run ``python -m bit_weight_quantization_moeq_amd.build`` (or call
 without a GPU.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -36,15 +38,27 @@ def hipcc():
     return exe
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stdout}\n{proc.stderr}")
+
+
+def build(verbose=False):
+    """Compile every source to an object in parallel, then link."""
+    hip = hipcc()
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="moeq_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hip, *compile_flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", "-o", o, os.path.join(CSRC, s)]
+                for s, o in zip(SOURCES, objs)]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([hip, *FLAGS, "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -36,6 +36,8 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     assert moeq.moeq_abi_version() == 2
+    m = re.search(r"#define\s+MOEQ_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == moeq.ABI_VERSION == moeq.moeq_abi_version()
     for s in range(0, -8, -1):
         assert moeq.moeq_status_string(s) != "unknown status"
     assert moeq.moeq_status_string(-99) == "unknown status"
@@ -150,3 +152,15 @@ def test_double_quant_validation_rejects_before_any_device_call():
     gu, dn = _qw(3, E, 2 * I, H, 64, c=1024), _qw(3, E, H, I, 64, c=2048)
     assert lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(dn)) > 0
     assert lib.moeq_experts_forward_workspace_bytes(10, 2, ctypes.byref(gu), ctypes.byref(_qw(1, E, H, I, 64))) == 0
+
+
+def test_graft_entry_build_checks_pass(monkeypatch):
+    """__graft_entry__.build() minus the compile: its checks on the built
+    library hold (the compile itself is exercised by calling build())."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import __graft_entry__
+    from bit_weight_quantization_moeq_amd import build as b
+    monkeypatch.setattr(b, "build", lambda verbose=False: moeq.library_path())
+    __graft_entry__.build()
