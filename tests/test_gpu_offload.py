@@ -1,6 +1,6 @@
 """Expert-granularity offload: the forward through pinned-host layers with a
 two-slot device cache and side-stream prefetch is bit-identical to the
-resident forward (the invariant the offload proposal is judged by), for
+resident forward (the invariant the offload proposal is measured against), for
 layer sequences that revisit layers and for both formats."""
 
 import pytest
