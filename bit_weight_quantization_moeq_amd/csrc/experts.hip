@@ -1110,10 +1110,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
 
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
     // this lane's half of step ks of the token row: K is a multiple of 64,
-    // so the half is wholly in range or wholly past the end (then row start)
-    // fragment s_ of this lane's half of step ks of the token row: K is a
-    // multiple of 64, so the half is wholly in range or wholly past the end
-    // (then the row start)
+    // so the half is wholly in range or wholly past the end (then the row
+    // start)
     auto bptr = [&](int ks) {
       const int kb = ks * kStep + (kStep / 2) * hh;
       return reinterpret_cast<const bf16x8*>(brow + (kb < K ? kb : 0));

@@ -4,6 +4,8 @@
     python -m bit_weight_quantization_moeq_amd.profsum stats <kernel_stats.csv> "<command>"
     python -m bit_weight_quantization_moeq_amd.profsum traffic <fetch_dir> <write_dir> <kernel> <copy_bytes> \
         <algorithmic_bytes> "<fetch command>" "<write command>"
+    python -m bit_weight_quantization_moeq_amd.profsum decode <kernel_trace.csv> <H> <I> \
+        <format>=<bytes_per_weight>[,...] <grid_x>=<touched experts>[,...] "<command>"
 
 ``stats`` prints a per-kernel duration table.  ``traffic`` reads two
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch), takes the
@@ -11,7 +13,9 @@ mean per dispatch of ``kernel`` and calibrates each counter against the
 largest plain device copy in the same run (``copy_bytes`` bytes read and
 written by ``__amd_rocclr_copyBuffer``), then prints the table plus a JSON
 block that bench.py reads; the block carries the SHA-256 of the kernel
-sources so that a changed kernel reports no stale traffic.
+sources so that a changed kernel reports no stale traffic.  ``decode`` splits
+the few-assignment kernels' dispatches by launch grid (one grid per batch
+size) and prices each against the packed bytes of the experts it touches.
 """
 
 import csv
@@ -102,10 +106,45 @@ def traffic(fetch_dir, write_dir, kernel, copy_bytes, algo_bytes, cmd_f, cmd_w):
     print("\n```json\n" + json.dumps(block) + "\n```")
 
 
+def decode(trace, H, I, bpw, grids, command):
+    """Per-launch-grid durations of the few-assignment kernels from a
+    --kernel-trace CSV, and GB/s over the touched experts' packed weights
+    (gate_up 2I x H for the G1 launch, down H x I for G2; bpw maps the
+    kernel's format tag, its first template argument, to packed bytes per
+    weight)."""
+    H, I = int(H), int(I)
+    bpw = {int(k): float(v) for k, v in (g.split("=") for g in bpw.split(","))}
+    touched = {int(k): int(v) for k, v in (g.split("=") for g in grids.split(","))}
+    groups = {}
+    for r in csv.DictReader(open(trace)):
+        name = short(r["Kernel_Name"])
+        if not name.startswith("decode"):
+            continue
+        key = (name, int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"command: `{command}`\n")
+    print("| kernel | grid (threads x, y) | touched experts | dispatches | avg us | min us | max us "
+          "| packed MB | GB/s (avg) |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
+    for (name, gx, gy), v in sorted(groups.items()):
+        avg = sum(v) / len(v)
+        u = touched.get(gx)
+        mb = gbs = ""
+        if u is not None and name.startswith("decode_kernel"):
+            args = name[name.index("<") + 1:].split(",")
+            g1 = args[1].strip() == "true"
+            b = u * (2 * I * H if g1 else H * I) * bpw[int(args[0])]
+            mb, gbs = f"{b / 1e6:.1f}", f"{b / avg / 1e3:.0f}"
+        print(f"| {name} | {gx} x {gy} | {'' if u is None else u} | {len(v)} | {avg:.2f} | {min(v):.2f} "
+              f"| {max(v):.2f} | {mb} | {gbs} |")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:9])
+    elif sys.argv[1] == "decode":
+        decode(*sys.argv[2:8])
     else:
         raise SystemExit(__doc__)
