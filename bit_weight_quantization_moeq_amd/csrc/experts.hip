@@ -367,6 +367,19 @@ struct StreamCodes {
     m = in ? 0xffffffffu : 0u;
     asm volatile("" : "+v"(m));  // opaque, so the select is not folded into a branch around the loads
   }
+  // The codes and the range mask only, for a caller that loads the scales
+  // itself and sets raw.scale before use().
+  __device__ __forceinline__ void fetch_codes(const uint8_t* row_base, int k0, int hh, int K, bool ok) {
+    constexpr int half = Fmt<FMT>::kStep / 2;
+    const int kk = k0 + half * hh;
+    const bool in = ok && kk < K;
+    const int kc = in ? kk : 0;
+    const uint4* p = reinterpret_cast<const uint4*>(row_base + (kNf4Codes<FMT> ? kc / 2 : kc));
+    raw.c0 = p[0];
+    raw.c1 = p[1];
+    m = in ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));
+  }
   __device__ __forceinline__ RowCodes<FMT> use() const {
     RowCodes<FMT> r = raw;
     r.m = m;
@@ -993,7 +1006,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int FMT, bool G1, int NW>
+template <int FMT, bool G1, int NW, bool PAIR>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restrict__ act,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ wts, int32_t n, int32_t Ktop,
@@ -1076,8 +1089,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     rs1 = s1.p[0];
   }
   StreamCodes<FMT> ca0, ca1, cb0, cb1;
-  ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1, rs0);
-  ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1, rs1);
+  // PAIR (plain NF4, an even number of 64-blocks per row): the absmax of two
+  // K steps comes in one 8-byte load per lane and row instead of two 4-byte
+  // ones.  Lanes of half hh load the pair of step ks + hh (blocks 2(ks+hh)
+  // and 2(ks+hh)+1; row start past the range); one v_permlane32_swap then
+  // gives every lane its own block of step ks and of step ks + 1.  Each such
+  // load touches one cache line per row of the wave, so halving their number
+  // shortens the step.
+  float2 pr0 = {}, pr1 = {};
+  auto fetch_pair = [&](int ks) {
+    if constexpr (PAIR) {
+      const int st = ks + hh;
+      const int b = st < ks1 ? 2 * st : 0;
+      pr0 = *reinterpret_cast<const float2*>(s0.p + b);
+      pr1 = *reinterpret_cast<const float2*>(s1.p + b);
+    }
+  };
+  auto fetch_step = [&](StreamCodes<FMT>& c0, StreamCodes<FMT>& c1, int ks) {
+    if constexpr (PAIR) {
+      c0.fetch_codes(q0, ks * kStep, hh, K, ks < ks1);
+      c1.fetch_codes(q1, ks * kStep, hh, K, ks < ks1);
+    } else {
+      c0.fetch(q0, s0, ks * kStep, hh, K, ks < ks1, rs0);
+      c1.fetch(q1, s1, ks * kStep, hh, K, ks < ks1, rs1);
+    }
+  };
+  fetch_step(ca0, ca1, ks0);
+  fetch_pair(ks0);
 
   // 4. the expert's assignments in ascending order: chunk c = a / 64 is
   //    wave c % NW's j = c / NW values
@@ -1104,8 +1142,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     const int a = list[tok];
     const uint16_t* brow = G1 ? act + (int64_t)(a / Ktop) * H : act + (int64_t)a * I;
     if (g > 0) {
-      ca0.fetch(q0, s0, ks0 * kStep, hh, K, ks0 < ks1, rs0);
-      ca1.fetch(q1, s1, ks0 * kStep, hh, K, ks0 < ks1, rs1);
+      fetch_step(ca0, ca1, ks0);
+      fetch_pair(ks0);
     }
 
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
@@ -1124,11 +1162,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     // the token fragments (L2 hits) are awaited.  Steps past the wave's range
     // load in-range addresses and are zeroed through their scale.
     bf16x8 xa[kS];
-    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1) {
+    float nx0 = 0.0f, nx1 = 0.0f;  // PAIR: the second step's absmax, after the swap
+    // second: the step is the second of its trip (ks - ks0 odd)
+    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, bool second) {
       // keep each step's arithmetic after the previous step's (hoisting it
       // would wait for codes that are still loading)
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8* pn = bptr(ks + 1);
+      if constexpr (PAIR) {
+        if (!second) {
+          const auto sw0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pr0.x), __float_as_uint(pr0.y), false, false);
+          const auto sw1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pr1.x), __float_as_uint(pr1.y), false, false);
+          sc0.raw.scale = {__uint_as_float(sw0[0])};
+          sc1.raw.scale = {__uint_as_float(sw1[0])};
+          nx0 = __uint_as_float(sw0[1]);
+          nx1 = __uint_as_float(sw1[1]);
+        } else {
+          sc0.raw.scale = {nx0};
+          sc1.raw.scale = {nx1};
+        }
+      }
       const RowCodes<FMT> c0 = sc0.use(), c1 = sc1.use();
       Dequant<FMT> d0, d1;
       d0.prepare(c0);
@@ -1139,16 +1192,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
         acc1 = mfma(d1.frag(c1, s_), xa[s_], acc1);
         xa[s_] = pn[s_];
       }
-      sc0.fetch(q0, s0, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs0);
-      sc1.fetch(q1, s1, (ks + 2) * kStep, hh, K, ks + 2 < ks1, rs1);
+      fetch_step(sc0, sc1, ks + 2);
+      if (!second) fetch_pair(ks + 2);
     };
     {
       const bf16x8* p0 = bptr(ks0);
 #pragma unroll
       for (int s_ = 0; s_ < kS; ++s_) xa[s_] = p0[s_];
     }
-    cb0.fetch(q0, s0, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs0);
-    cb1.fetch(q1, s1, (ks0 + 1) * kStep, hh, K, ks0 + 1 < ks1, rs1);
+    fetch_step(cb0, cb1, ks0 + 1);
     // Two steps per trip, register sets alternating, with no branch between
     // them (a branch there would make the compiler copy or re-load register
     // sets that are still loading, forcing full waits).  Parts are whole
@@ -1156,8 +1208,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     // trailing step past the range: its scale is zero, its A operand exactly
     // zero, and it adds nothing.
     for (int ks = ks0; ks < ks1; ks += 2) {
-      kstep(ks, ca0, ca1);
-      kstep(ks + 1, cb0, cb1);
+      kstep(ks, ca0, ca1, false);
+      kstep(ks + 1, cb0, cb1, true);
     }
 
     // the P partial sums of each row block, added in part order
@@ -1658,8 +1710,14 @@ void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const
                         const uint8_t* scc, hipStream_t s) {
   const int32_t n = a.T * a.K;
   const DecodeShape d = decode_shape(ux, G1 ? a.I / 32 : a.H / 64);
-  decode_kernel<FMT, G1, kWaves><<<dim3(ux, d.gy), kThreads, 0, s>>>(act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p,
-                                                                     q, sc, scc, a.h, a.y);
+  bool pair = false;
+  if constexpr (FMT == MOEQ_FMT_NF4) pair = ((G1 ? a.H : a.I) / kNf4Block) % 2 == 0;
+  if (pair)
+    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
+  else
+    decode_kernel<FMT, G1, kWaves, false><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
 }
 
 template <int FMT>

@@ -84,6 +84,22 @@ def test_forward_workloads_sampled(name, T, ns, nc):
     assert torch.isfinite(out.float()).all()
 
 
+# NF4 rows with an odd number of 64-blocks (H = 320: 5, I = 192: 3) and with
+# an even number that is not a multiple of 4 (H = 384: 6, I = 128: 2): the
+# few-assignment path loads the absmax of two K steps at once only when the
+# count is even.  T*K = 2 and 32 take the few-assignment path, 600 the tiled one.
+@pytest.mark.parametrize("H,I", [(320, 192), (384, 128)])
+@pytest.mark.parametrize("T", [1, 16, 300])
+def test_forward_nf4_block_counts(H, I, T):
+    s = syn.MoEShape("blocks", E=4, H=H, I=I, K=2, fmt="nf4")
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    say(f"forward nf4 H={H} I={I} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu), moeq.moeq_quantize_nf4(dn)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    torch.cuda.synchronize()
+    _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"nf4 H={H} I={I} T={T}")
+
+
 # T*K = 387 takes the few-assignment path, 900 the tiled one
 @pytest.mark.parametrize("T", [129, 300])
 @pytest.mark.parametrize("fmt", ["nf4", "int8"])
