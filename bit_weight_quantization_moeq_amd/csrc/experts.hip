@@ -1156,8 +1156,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     };
     // One K step: multiply this step's token fragments, each one replaced
     // by the next step's as soon as its two MFMAs have issued (one register
-    // set, so the kernel stays within three waves' worth of registers per
-    // SIMD), then refill this step's code registers two steps ahead.  Loads
+    // set: 132 VGPRs, three waves per SIMD; the PAIR form needs 152, two
+    // waves), then refill this step's code registers two steps ahead.  Loads
     // complete in issue order, so codes stay in flight across a step while
     // the token fragments (L2 hits) are awaited.  Steps past the wave's range
     // load in-range addresses and are zeroed through their scale.
