@@ -62,6 +62,23 @@ def test_backward_tiny_full(fmt):
     _compare(x, idx, wts, gu, dn, dout, fmt, gx, gw, np.arange(64), f"tiny {fmt}")
 
 
+# NF4 rows with an odd number of 64-blocks (H = 320, I = 192) and with an even
+# number that is not a multiple of 4 (H = 384, I = 128): ragged column tiles in
+# the transposed GEMMs.
+@pytest.mark.parametrize("H,I", [(320, 192), (384, 128)])
+def test_backward_nf4_block_counts(H, I):
+    s = syn.MoEShape("blocks", E=4, H=H, I=I, K=2, fmt="nf4")
+    T = 200
+    gu, dn, x, idx, wts = syn.layer_inputs(s, T, device="cpu")
+    dout = syn.grad_output(T, s.H, device="cpu")
+    gu, dn, x, idx, wts, dout = (t.cuda() for t in (gu, dn, x, idx, wts, dout))
+    say(f"backward nf4 H={H} I={I} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu), moeq.moeq_quantize_nf4(dn)
+    gx, gw = moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout)
+    torch.cuda.synchronize()
+    _compare(x, idx, wts, gu, dn, dout, "nf4", gx, gw, np.arange(T), f"nf4 H={H} I={I}")
+
+
 # (shape, T, sampled tokens): gpt-oss has an odd number of 64-row K steps in
 # the down-projection transpose (H = 2880)
 CASES = [("olmoe", 512, 3), ("qwen3", 256, 3), ("gptoss", 64, 3), ("mixtral", 32, 2)]
