@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-offload", action="store_true")
     ap.add_argument("--no-double-quant", action="store_true")
     ap.add_argument("--no-load", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the experts forward at every configured shape and batch (off by default)")
     return ap.parse_args()
 
 
@@ -416,6 +418,47 @@ def codec_figures(torch, np, moeq, syn, dev, copy_GBps, reps=5):
     return out
 
 
+def configs_figures(torch, moeq, syn, dev, reps=20):
+    """The experts forward at every configured shape and batch size: the
+    shape's format, weights quantized on the device, 20 back-to-back calls
+    between one pair of events (routing included); TFLOP/s over 6 T K H I and
+    GB/s over the touched experts' packed weights."""
+    out = []
+    for name, s in syn.SHAPES.items():
+        if name == "tiny":
+            continue
+        gu = syn.expert_weights(s.gate_up_shape, tensor=syn.GATE_UP, outliers=s.outliers, device=dev)
+        dn = syn.expert_weights(s.down_shape, tensor=syn.DOWN, outliers=s.outliers, device=dev)
+        quant = moeq.moeq_quantize_nf4 if s.fmt == "nf4" else moeq.moeq_quantize_int8_rowwise
+        qg, qd = quant(gu), quant(dn)
+        del gu, dn
+        bpe = NF4_PACKED_BYTES_PER_ELEM if s.fmt == "nf4" else 1.0
+        for T in s.tokens:
+            x = syn.hidden_states(T, s.H, device=dev)
+            idx, wts = syn.routing(T, s.K, s.E, kind=s.routing, device=dev)
+            o = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=o, workspace=ws)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                moeq.moeq_experts_forward(x, idx, wts, qg, qd, out=o, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            flops = 6.0 * T * s.K * s.H * s.I
+            u = int(torch.unique(idx[(idx >= 0) & (idx < s.E)]).numel())
+            packed = u * 3.0 * s.H * s.I * bpe
+            out.append({"config": name, "format": s.fmt, "T": T, "forward_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                        "TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                        "touched_experts": u, "packed_GBps": packed / (ms * 1e-3) / 1e9})
+            del x, idx, wts, o, ws
+        del qg, qd
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -565,6 +608,9 @@ def main():
         result["codec"] = codec_figures(torch, np, moeq, syn, dev, copy_GBps)
     if not args.no_load:
         result["load"] = load_figures(torch, np, moeq, syn, dev, copy_GBps)
+
+    if args.configs:
+        result["configs"] = configs_figures(torch, moeq, syn, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, gu, dn, x, idx, wts, T)
