@@ -143,3 +143,33 @@ def test_copy_async_carries_absmax_codes():
     torch.cuda.synchronize()
     for a, b in zip(q._tensors(), back._tensors()):
         assert torch.equal(a, b)
+
+
+# Rows with an odd block count (H = 320: 5 blocks, I = 192: 3) and an even one
+# that is not a multiple of 4 (H = 384, I = 128): 256-block scale groups start
+# mid-row, and the plain-NF4 twin takes the paired-absmax decode kernel where
+# the block count is even.  T*K = 32 takes the few-assignment path, 600 the
+# tiled one; the backward is always tiled.
+@pytest.mark.parametrize("H,I", [(320, 192), (384, 128)])
+@pytest.mark.parametrize("T", [16, 300])
+def test_double_quant_block_counts(H, I, T):
+    s = syn.MoEShape("blocks", E=4, H=H, I=I, K=2, fmt="nf4")
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    dout = syn.grad_output(T, H, device="cuda")
+    say(f"dq block counts H={H} I={I} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu, double_quant=True), moeq.moeq_quantize_nf4(dn, double_quant=True)
+    tg, td = _decoded_nf4(qg), _decoded_nf4(qd)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    twin = moeq.moeq_experts_forward(x, idx, wts, tg, td)
+    gx, gw = moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout)
+    tx, tw = moeq.moeq_experts_backward(x, idx, wts, tg, td, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), twin.view(torch.int16))
+    assert torch.equal(gx.view(torch.int16), tx.view(torch.int16))
+    assert torch.equal(gw, tw)
+    tokens = np.arange(T)
+    ref = experts_forward(host_bits(x)[tokens], host(idx)[tokens], host(wts)[tokens], LazyDequant(gu, "nf4_dq"),
+                          LazyDequant(dn, "nf4_dq"))
+    err = rel_frobenius(bf16_to_f32(host_bits(out)[tokens]).astype(np.float64), ref)
+    print(f"dq H={H} I={I} T={T}: rel Frobenius error {err:.3e}")
+    assert err <= TOL
