@@ -87,7 +87,7 @@ def measured_traffic(stage):
     import glob
     import re
 
-    from bit_weight_quantization_moeq_amd.profsum import source_hash
+    from profsum import source_hash
     want = PROFILE_KERNEL.get(stage)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
         m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)

@@ -104,14 +104,82 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _dev(t, dtype, name):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+def _dev(t, dtype, name, shape=None):
+    """Structural check of a caller tensor before its pointer reaches the
+    library: exact shape (when given), dtype and contiguity.  The C side sees
+    only raw pointers and trusts the sizes it is given, so a wrong-sized
+    buffer must be refused here, loudly, rather than read or written out of
+    bounds.  Where the tensors live is checked once per call, after every
+    structural check (:func:`_on_device`)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if shape is not None and tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _on_device(where, *tensors):
+    """Every tensor is a CUDA (HIP) tensor, all on one device."""
+    ts = [t for t in tensors if t is not None]
+    for t in ts:
+        if not t.is_cuda:
+            raise TypeError(f"{where}: every tensor must be a CUDA (HIP) tensor")
+    if len({t.device for t in ts}) > 1:
+        raise ValueError(f"{where}: tensors on different devices {sorted({str(t.device) for t in ts})}")
+
+
+def _match_qweight(q, shape, formats, name):
+    """q is a QWeight of one of ``formats`` describing ``shape`` [E, rows, cols]."""
+    if not isinstance(q, QWeight):
+        raise TypeError(f"{name} must be a QWeight")
+    if q.format not in formats:
+        raise ValueError(f"{name} has format {q.format}, expected one of {formats}")
+    if tuple(q.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} describes {tuple(q.shape)}, expected {tuple(shape)}")
+
+
+def _forward_weights(gate_up, down, H):
+    """gate_up [E, 2I, H] and down [E, H, I]: each checked against its own
+    layout and the hidden width H (the library derives H from gate_up; whether
+    the two tensors fit each other is the library's own check)."""
+    for name, q in (("gate_up", gate_up), ("down", down)):
+        if not isinstance(q, QWeight):
+            raise TypeError(f"{name} must be a QWeight")
+        q.validate_layout()
+    if gate_up.cols != H:
+        raise ValueError(f"hidden width {H} must equal gate_up cols ({gate_up.cols})")
+    return gate_up._tensors() + down._tensors()
+
+
+def _routed_inputs(hidden, top_k_index, top_k_weights):
+    """(T, H, K) of hidden [T, H] bf16, top_k_index [T, K] int32 and
+    top_k_weights [T, K] fp32, structurally checked."""
+    for name, t in (("hidden", hidden), ("top_k_index", top_k_index), ("top_k_weights", top_k_weights)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
+    T, H = hidden.shape
+    K = top_k_index.shape[1]
+    _dev(hidden, torch.bfloat16, "hidden")
+    _dev(top_k_index, torch.int32, "top_k_index", (T, K))
+    _dev(top_k_weights, torch.float32, "top_k_weights", (T, K))
+    return int(T), int(H), int(K)
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (a uint8 device tensor, size checked by the
+    library) or a new one of ``need`` bytes."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+    _on_device("workspace", workspace)
+    if workspace.device != device:
+        raise ValueError("workspace must be on the device of the activations")
+    return workspace
 
 
 class QWeight:
@@ -172,7 +240,56 @@ class QWeight:
         codes = new[2] if len(new) == 3 else None
         return QWeight(self.format, self.num_experts, self.rows, self.cols, new[0], new[1], codes)
 
-    def _c(self):
+    def layout(self):
+        """``[(name, shape, dtype)]`` of the tensors this format and shape need."""
+        E, R, C = self.num_experts, self.rows, self.cols
+        if self.format in (FMT_NF4, FMT_NF4_DQ):
+            nb = R * (C // NF4_BLOCKSIZE)
+            lay = [("qdata", (E, R, C // 2), torch.uint8)]
+            if self.format == FMT_NF4:
+                return lay + [("scales", (E, nb), torch.float32)]
+            return lay + [("scales", (E, (nb + DQ_GROUP - 1) // DQ_GROUP), torch.float32),
+                          ("scale_codes", (E, nb), torch.uint8)]
+        if self.format == FMT_INT8_ROWWISE:
+            return [("qdata", (E, R, C), torch.int8), ("scales", (E, R), torch.float32)]
+        raise ValueError(f"unknown format {self.format}")
+
+    def validate_layout(self):
+        """Every tensor has exactly the size and dtype that the format and
+        shape need and is contiguous.  Raises ValueError / TypeError."""
+        if self.format in (FMT_NF4, FMT_NF4_DQ) and self.cols % NF4_BLOCKSIZE != 0:
+            raise ValueError(f"NF4 needs cols % {NF4_BLOCKSIZE} == 0, got cols={self.cols}")
+        lay = self.layout()
+        if self.format != FMT_NF4_DQ and self.scale_codes is not None:
+            raise ValueError("scale_codes is only used by the double-quantized NF4 format")
+        for name, shape, dtype in lay:
+            t = getattr(self, name)
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"QWeight.{name} must be a torch tensor")
+            if t.numel() != int(torch.Size(shape).numel()):
+                raise ValueError(f"QWeight.{name} must hold {shape} ({torch.Size(shape).numel()} elements), "
+                                 f"got {tuple(t.shape)}")
+            if t.dtype != dtype:
+                raise TypeError(f"QWeight.{name} must be {dtype}, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"QWeight.{name} must be contiguous")
+        return self
+
+    def validate(self, allow_host=False):
+        """validate_layout(), and every tensor on one device: a CUDA device,
+        or pinned host memory when ``allow_host``."""
+        self.validate_layout()
+        ts = self._tensors()
+        for t in ts:
+            if not t.is_cuda and not (allow_host and t.device.type == "cpu" and t.is_pinned()):
+                raise TypeError("QWeight tensors must be CUDA (HIP) tensors"
+                                + (" or pinned host memory" if allow_host else ""))
+        if len({t.device for t in ts}) > 1:
+            raise ValueError("QWeight tensors on different devices")
+        return self
+
+    def _c(self, allow_host=False):
+        self.validate(allow_host)
         codes = self.scale_codes.data_ptr() if self.scale_codes is not None else None
         return _QW(self.format, self.num_experts, self.rows, self.cols, self.blocksize,
                    self.qdata.data_ptr(), self.scales.data_ptr(), codes)
@@ -196,10 +313,14 @@ def moeq_quantize_nf4(w, out=None, stream=None, double_quant=False):
     """bf16 ``[E, rows, cols]`` -> NF4 :class:`QWeight` (blocksize 64), with
     the absmax double-quantized when ``double_quant`` (or ``out`` has that
     format)."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        raise ValueError("w must be a [E, rows, cols] tensor")
     _dev(w, torch.bfloat16, "w")
-    if w.dim() != 3:
-        raise ValueError("w must be [E, rows, cols]")
     fmt = FMT_NF4_DQ if double_quant else FMT_NF4
+    if out is not None:
+        _match_qweight(out, tuple(w.shape), (FMT_NF4, FMT_NF4_DQ), "out")
+        out.validate_layout()
+    _on_device("moeq_quantize_nf4", w, *(out._tensors() if out is not None else []))
     q = out if out is not None else QWeight.empty(fmt, *w.shape, device=w.device)
     qc = q._c()
     _check(_load().moeq_quantize_nf4(_ptr(w), ctypes.byref(qc), _stream(stream)), "moeq_quantize_nf4")
@@ -210,8 +331,12 @@ def moeq_compress_absmax(src, out=None, share_codes=True, stream=None):
     """NF4 :class:`QWeight` -> the same weights with double-quantized absmax.
     With ``share_codes`` the result uses ``src.qdata`` itself; otherwise the
     packed codes are copied into ``out`` (or a new buffer)."""
-    if src.format != FMT_NF4:
-        raise ValueError("moeq_compress_absmax takes an NF4 QWeight")
+    _match_qweight(src, src.shape, (FMT_NF4,), "src")
+    src.validate_layout()
+    if out is not None:
+        _match_qweight(out, src.shape, (FMT_NF4_DQ,), "out")
+        out.validate_layout()
+    _on_device("moeq_compress_absmax", *src._tensors(), *(out._tensors() if out is not None else []))
     if out is None:
         out = QWeight.empty(FMT_NF4_DQ, *src.shape, device=src.qdata.device)
         if share_codes:
@@ -224,9 +349,13 @@ def moeq_compress_absmax(src, out=None, share_codes=True, stream=None):
 
 def moeq_quantize_int8_rowwise(w, out=None, stream=None):
     """bf16 ``[E, rows, cols]`` -> row-wise int8 :class:`QWeight`."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        raise ValueError("w must be a [E, rows, cols] tensor")
     _dev(w, torch.bfloat16, "w")
-    if w.dim() != 3:
-        raise ValueError("w must be [E, rows, cols]")
+    if out is not None:
+        _match_qweight(out, tuple(w.shape), (FMT_INT8_ROWWISE,), "out")
+        out.validate_layout()
+    _on_device("moeq_quantize_int8_rowwise", w, *(out._tensors() if out is not None else []))
     q = out if out is not None else QWeight.empty(FMT_INT8_ROWWISE, *w.shape, device=w.device)
     qc = q._c()
     _check(_load().moeq_quantize_int8_rowwise(_ptr(w), ctypes.byref(qc), _stream(stream)),
@@ -236,16 +365,21 @@ def moeq_quantize_int8_rowwise(w, out=None, stream=None):
 
 def moeq_dequantize(q, out=None, stream=None):
     """:class:`QWeight` -> bf16 ``[E, rows, cols]``."""
+    if not isinstance(q, QWeight):
+        raise TypeError("q must be a QWeight")
+    q.validate_layout()
+    if out is not None:
+        _dev(out, torch.bfloat16, "out", q.shape)
+    _on_device("moeq_dequantize", *q._tensors(), out)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.qdata.device)
-    _dev(out, torch.bfloat16, "out")
     qc = q._c()
     _check(_load().moeq_dequantize(ctypes.byref(qc), _ptr(out), _stream(stream)), "moeq_dequantize")
     return out
 
 
 def moeq_experts_forward_workspace_bytes(T, K, gate_up, down):
-    gu, dn = gate_up._c(), down._c()
+    gu, dn = gate_up._c(allow_host=True), down._c(allow_host=True)
     return int(_load().moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
 
 
@@ -256,23 +390,17 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
     ``stage_events``: optional sequence of 5 raw hipEvent_t handles (ints),
     recorded at the stage boundaries (``moeq_experts_forward_timed``).
     """
-    _dev(hidden, torch.bfloat16, "hidden")
-    _dev(top_k_index, torch.int32, "top_k_index")
-    _dev(top_k_weights, torch.float32, "top_k_weights")
-    T, H = hidden.shape
-    K = top_k_index.shape[1]
-    if tuple(top_k_index.shape) != (T, K) or tuple(top_k_weights.shape) != (T, K):
-        raise ValueError("top_k_index and top_k_weights must both be [T, K]")
+    T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
+    if out is not None:
+        _dev(out, torch.bfloat16, "out", (T, H))
+    wt = _forward_weights(gate_up, down, H)
+    _on_device("moeq_experts_forward", hidden, top_k_index, top_k_weights, out, *wt)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
-    _dev(out, torch.bfloat16, "out")
-    if out.shape[0] != T or out.shape[1] != gate_up.cols or H != gate_up.cols:
-        raise ValueError("hidden / out width must equal gate_up cols (H)")
     gu, dn = gate_up._c(), down._c()
     lib = _load()
     need = int(lib.moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    workspace = _workspace(workspace, need, hidden.device)
     args = (_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K), ctypes.byref(gu),
             ctypes.byref(dn), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     if stage_events is None:
@@ -286,7 +414,7 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
 
 
 def moeq_experts_backward_workspace_bytes(T, K, gate_up, down):
-    gu, dn = gate_up._c(), down._c()
+    gu, dn = gate_up._c(allow_host=True), down._c(allow_host=True)
     return int(_load().moeq_experts_backward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
 
 
@@ -296,27 +424,23 @@ def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, gra
     ``top_k_weights`` (packed weights frozen) for the incoming gradient
     ``grad_out`` (bf16 ``[T, H]``); returns ``(grad_hidden bf16 [T, H],
     grad_weights fp32 [T, K])``."""
-    _dev(hidden, torch.bfloat16, "hidden")
-    _dev(top_k_index, torch.int32, "top_k_index")
-    _dev(top_k_weights, torch.float32, "top_k_weights")
-    _dev(grad_out, torch.bfloat16, "grad_out")
-    T, H = hidden.shape
-    K = top_k_index.shape[1]
-    if tuple(top_k_index.shape) != (T, K) or tuple(top_k_weights.shape) != (T, K):
-        raise ValueError("top_k_index and top_k_weights must both be [T, K]")
-    if tuple(grad_out.shape) != (T, H) or H != gate_up.cols:
-        raise ValueError("grad_out must be [T, H] with H = gate_up cols")
+    T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
+    _dev(grad_out, torch.bfloat16, "grad_out", (T, H))
+    if grad_hidden is not None:
+        _dev(grad_hidden, torch.bfloat16, "grad_hidden", (T, H))
+    if grad_weights is not None:
+        _dev(grad_weights, torch.float32, "grad_weights", (T, K))
+    wt = _forward_weights(gate_up, down, H)
+    _on_device("moeq_experts_backward", hidden, top_k_index, top_k_weights, grad_out, grad_hidden,
+               grad_weights, *wt)
     if grad_hidden is None:
         grad_hidden = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
     if grad_weights is None:
         grad_weights = torch.empty((T, K), dtype=torch.float32, device=hidden.device)
-    _dev(grad_hidden, torch.bfloat16, "grad_hidden")
-    _dev(grad_weights, torch.float32, "grad_weights")
     gu, dn = gate_up._c(), down._c()
     lib = _load()
     need = int(lib.moeq_experts_backward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    workspace = _workspace(workspace, need, hidden.device)
     _check(lib.moeq_experts_backward(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
                                      ctypes.byref(gu), ctypes.byref(dn), _ptr(grad_out), _ptr(grad_hidden),
                                      _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -327,18 +451,26 @@ def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, gra
 def moeq_router_topk(hidden, gate, K, renormalize=False, top_k_index=None, top_k_weights=None, stream=None):
     """Router front-end: ``hidden`` bf16 ``[T, H]``, ``gate`` bf16 ``[E, H]`` ->
     ``(top_k_index int32 [T, K], top_k_weights fp32 [T, K])``."""
-    _dev(hidden, torch.bfloat16, "hidden")
-    _dev(gate, torch.bfloat16, "gate")
+    if not isinstance(hidden, torch.Tensor) or hidden.dim() != 2:
+        raise ValueError("hidden must be a [T, H] tensor")
     T, H = hidden.shape
-    E = gate.shape[0]
-    if gate.dim() != 2 or gate.shape[1] != H:
+    _dev(hidden, torch.bfloat16, "hidden")
+    if not isinstance(gate, torch.Tensor) or gate.dim() != 2 or gate.shape[1] != H:
         raise ValueError("gate must be [E, H]")
+    _dev(gate, torch.bfloat16, "gate")
+    E = gate.shape[0]
+    K = int(K)
+    if K < 1:
+        raise ValueError("K must be >= 1")
+    if top_k_index is not None:
+        _dev(top_k_index, torch.int32, "top_k_index", (T, K))
+    if top_k_weights is not None:
+        _dev(top_k_weights, torch.float32, "top_k_weights", (T, K))
+    _on_device("moeq_router_topk", hidden, gate, top_k_index, top_k_weights)
     if top_k_index is None:
-        top_k_index = torch.empty((T, int(K)), dtype=torch.int32, device=hidden.device)
+        top_k_index = torch.empty((T, K), dtype=torch.int32, device=hidden.device)
     if top_k_weights is None:
-        top_k_weights = torch.empty((T, int(K)), dtype=torch.float32, device=hidden.device)
-    _dev(top_k_index, torch.int32, "top_k_index")
-    _dev(top_k_weights, torch.float32, "top_k_weights")
+        top_k_weights = torch.empty((T, K), dtype=torch.float32, device=hidden.device)
     _check(_load().moeq_router_topk(_ptr(hidden), _ptr(gate), int(T), int(H), int(E), int(K),
                                     1 if renormalize else 0, _ptr(top_k_index), _ptr(top_k_weights),
                                     _stream(stream)), "moeq_router_topk")
@@ -349,10 +481,12 @@ def moeq_qweight_copy_async(src, dst, stream=None):
     """Asynchronous copy of a packed tensor between pinned host and device
     memory (either direction) on ``stream`` (default: torch's current)."""
     for name, q in (("source", src), ("destination", dst)):
+        if not isinstance(q, QWeight):
+            raise TypeError(f"{name} must be a QWeight")
         for t in q._tensors():
             if t.device.type == "cpu" and not t.is_pinned():
                 raise ValueError(f"host {name} must be pinned")
-    s, d = src._c(), dst._c()
+    s, d = src._c(allow_host=True), dst._c(allow_host=True)
     _check(_load().moeq_qweight_copy_async(ctypes.byref(s), ctypes.byref(d), _stream(stream)),
            "moeq_qweight_copy_async")
     return dst
@@ -367,7 +501,10 @@ def moeq_route_buckets(top_k_index, num_experts, workspace=None, stream=None):
 
     ``perm`` entries past ``offsets[E]`` (unrouted assignments) are -1 here.
     """
+    if not isinstance(top_k_index, torch.Tensor) or top_k_index.dim() != 2:
+        raise ValueError("top_k_index must be a [T, K] tensor")
     _dev(top_k_index, torch.int32, "top_k_index")
+    _on_device("moeq_route_buckets", top_k_index)
     T, K = top_k_index.shape
     E = int(num_experts)
     dev = top_k_index.device
@@ -377,8 +514,7 @@ def moeq_route_buckets(top_k_index, num_experts, workspace=None, stream=None):
     slot = torch.empty(T * K, dtype=torch.int32, device=dev)
     lib = _load()
     need = int(lib.moeq_route_workspace_bytes(int(T), int(K), E))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.moeq_route_buckets(_ptr(top_k_index), int(T), int(K), E, _ptr(counts), _ptr(offsets),
                                   _ptr(perm), _ptr(slot), _ptr(workspace), workspace.numel(),
                                   _stream(stream)), "moeq_route_buckets")

@@ -1,10 +1,10 @@
 """Condense rocprofv3 CSV output into the short Markdown summaries kept under
 ``profiles/``.
 
-    python -m bit_weight_quantization_moeq_amd.profsum stats <kernel_stats.csv> "<command>"
-    python -m bit_weight_quantization_moeq_amd.profsum traffic <fetch_dir> <write_dir> <kernel> <copy_bytes> \
+    python profsum.py stats <kernel_stats.csv> "<command>"
+    python profsum.py traffic <fetch_dir> <write_dir> <kernel> <copy_bytes> \
         <algorithmic_bytes> "<fetch command>" "<write command>"
-    python -m bit_weight_quantization_moeq_amd.profsum decode <kernel_trace.csv> <H> <I> \
+    python profsum.py decode <kernel_trace.csv> <H> <I> \
         <format>=<bytes_per_weight>[,...] <grid_x>=<touched experts>[,...] "<command>"
 
 ``stats`` prints a per-kernel duration table.  ``traffic`` reads two
@@ -26,7 +26,9 @@ import os
 import re
 import sys
 
-SOURCES = ("csrc/experts.hip", "csrc/quant.hip", "csrc/route.hip", "csrc/api.hip", "csrc/moeq_internal.h")
+PKG = "bit_weight_quantization_moeq_amd"
+SOURCES = tuple(f"{PKG}/csrc/{n}" for n in (
+    "experts.hip", "quant.hip", "route.hip", "api.hip", "router.hip", "moeq_internal.h"))
 
 
 def _code_only(text):

@@ -6,7 +6,7 @@ small synthetic CSVs with hand-computed answers."""
 import csv
 import json
 
-from bit_weight_quantization_moeq_amd import profsum
+import profsum
 
 TRACE_COLS = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y"]
 
