@@ -22,6 +22,7 @@ __all__ = [
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
     "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
     "moeq_qweight_copy_async", "FMT_NF4_DQ", "DQ_GROUP", "moeq_compress_absmax",
+    "moeq_stream_reference", "moeq_router_route", "moeq_experts_forward_routed", "Routing",
 ]
 
 FMT_NF4 = 1
@@ -29,7 +30,7 @@ FMT_INT8_ROWWISE = 2
 FMT_NF4_DQ = 3
 NF4_BLOCKSIZE = 64
 DQ_GROUP = 256
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libmoeq.so")
@@ -69,6 +70,7 @@ def _load():
         "moeq_nf4_codebook": (I32, [ctypes.POINTER(ctypes.c_float)]),
         "moeq_quantize_nf4": (I32, [P, QP, P]),
         "moeq_quantize_int8_rowwise": (I32, [P, QP, P]),
+        "moeq_stream_reference": (I32, [P, QP, P]),
         "moeq_compress_absmax": (I32, [QP, QP, P]),
         "moeq_dequantize": (I32, [QP, P, P]),
         "moeq_experts_forward_workspace_bytes": (SZ, [I32, I32, QP, QP]),
@@ -80,6 +82,9 @@ def _load():
         "moeq_router_topk": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P]),
         "moeq_qweight_copy_async": (I32, [QP, QP, P]),
         "moeq_route_buckets": (I32, [P, I32, I32, I32, P, P, P, P, P, SZ, P]),
+        "moeq_router_route_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "moeq_router_route": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P]),
+        "moeq_experts_forward_routed": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -327,6 +332,22 @@ def moeq_quantize_nf4(w, out=None, stream=None, double_quant=False):
     return q
 
 
+def moeq_stream_reference(w, out):
+    """Measurement reference (not part of the method): the bytes and launch
+    of :func:`moeq_quantize_nf4` into the plain NF4 ``out`` with no NF4
+    arithmetic; what it writes is meaningless.  Its rate is the attainable
+    bandwidth for the quantize kernel's byte mix and access pattern."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        raise ValueError("w must be a [E, rows, cols] tensor")
+    _dev(w, torch.bfloat16, "w")
+    _match_qweight(out, tuple(w.shape), (FMT_NF4,), "out")
+    out.validate_layout()
+    _on_device("moeq_stream_reference", w, *out._tensors())
+    qc = out._c()
+    _check(_load().moeq_stream_reference(_ptr(w), ctypes.byref(qc), _stream(None)), "moeq_stream_reference")
+    return out
+
+
 def moeq_compress_absmax(src, out=None, share_codes=True, stream=None):
     """NF4 :class:`QWeight` -> the same weights with double-quantized absmax.
     With ``share_codes`` the result uses ``src.qdata`` itself; otherwise the
@@ -475,6 +496,78 @@ def moeq_router_topk(hidden, gate, K, renormalize=False, top_k_index=None, top_k
                                     1 if renormalize else 0, _ptr(top_k_index), _ptr(top_k_weights),
                                     _stream(stream)), "moeq_router_topk")
     return top_k_index, top_k_weights
+
+
+class Routing:
+    """The grouping of T*K assignments by expert: ``counts`` [E],
+    ``offsets`` [E+1], ``perm`` [T*K] and ``slot`` [T*K] int32 device tensors
+    (as :func:`moeq_route_buckets` returns them)."""
+
+    def __init__(self, counts, offsets, perm, slot):
+        self.counts, self.offsets, self.perm, self.slot = counts, offsets, perm, slot
+
+    def __iter__(self):
+        return iter((self.counts, self.offsets, self.perm, self.slot))
+
+
+def moeq_router_route(hidden, gate, K, renormalize=False, workspace=None, stream=None):
+    """Router front-end fused with the routing stage: ``hidden`` bf16
+    ``[T, H]``, ``gate`` bf16 ``[E, H]`` -> ``(top_k_index int32 [T, K],
+    top_k_weights fp32 [T, K], Routing)``; the same as
+    :func:`moeq_router_topk` then :func:`moeq_route_buckets`."""
+    if not isinstance(hidden, torch.Tensor) or hidden.dim() != 2:
+        raise ValueError("hidden must be a [T, H] tensor")
+    T, H = hidden.shape
+    _dev(hidden, torch.bfloat16, "hidden")
+    if not isinstance(gate, torch.Tensor) or gate.dim() != 2 or gate.shape[1] != H:
+        raise ValueError("gate must be [E, H]")
+    _dev(gate, torch.bfloat16, "gate")
+    _on_device("moeq_router_route", hidden, gate)
+    E, K = int(gate.shape[0]), int(K)
+    if K < 1:
+        raise ValueError("K must be >= 1")
+    dev = hidden.device
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    r = Routing(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+                torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev))
+    lib = _load()
+    need = int(lib.moeq_router_route_workspace_bytes(int(T), int(H), E, K))
+    workspace = _workspace(workspace, need, dev)
+    _check(lib.moeq_router_route(_ptr(hidden), _ptr(gate), int(T), int(H), E, K, 1 if renormalize else 0,
+                                 _ptr(idx), _ptr(wts), _ptr(r.counts), _ptr(r.offsets), _ptr(r.perm),
+                                 _ptr(r.slot), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moeq_router_route")
+    return idx, wts, r
+
+
+def moeq_experts_forward_routed(hidden, top_k_index, top_k_weights, gate_up, down, routing, out=None,
+                                workspace=None, stream=None):
+    """:func:`moeq_experts_forward` with ``routing`` (a :class:`Routing` of
+    this top_k_index) supplied, so the routing stage is skipped."""
+    T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
+    if not isinstance(routing, Routing):
+        raise TypeError("routing must be a Routing")
+    E = gate_up.num_experts if isinstance(gate_up, QWeight) else 0
+    _dev(routing.offsets, torch.int32, "routing.offsets", (E + 1,))
+    _dev(routing.perm, torch.int32, "routing.perm", (T * K,))
+    _dev(routing.slot, torch.int32, "routing.slot", (T * K,))
+    if out is not None:
+        _dev(out, torch.bfloat16, "out", (T, H))
+    wt = _forward_weights(gate_up, down, H)
+    _on_device("moeq_experts_forward_routed", hidden, top_k_index, top_k_weights, out, routing.offsets,
+               routing.perm, routing.slot, *wt)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    gu, dn = gate_up._c(), down._c()
+    lib = _load()
+    need = int(lib.moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, hidden.device)
+    _check(lib.moeq_experts_forward_routed(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
+                                           ctypes.byref(gu), ctypes.byref(dn), _ptr(routing.offsets),
+                                           _ptr(routing.perm), _ptr(routing.slot), _ptr(out), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "moeq_experts_forward_routed")
+    return out
 
 
 def moeq_qweight_copy_async(src, dst, stream=None):

@@ -159,6 +159,15 @@ moeq_status moeq_quantize_nf4(const uint16_t* w, const moeq_qweight* dst, void* 
   return device_status(launch_quantize_nf4(w, static_cast<uint8_t*>(dst->qdata), dst->scales, nblocks, s));
 }
 
+moeq_status moeq_stream_reference(const uint16_t* w, const moeq_qweight* dst, void* stream) {
+  moeq_status st = check_qweight(dst, MOEQ_FMT_NF4);
+  if (st != MOEQ_OK) return st;
+  if (!w) return MOEQ_EINVAL;
+  if (!aligned16(w)) return MOEQ_EALIGN;
+  return device_status(launch_stream_reference(w, static_cast<uint8_t*>(dst->qdata), dst->scales,
+                                               numel(dst) / kNf4Block, static_cast<hipStream_t>(stream)));
+}
+
 moeq_status moeq_compress_absmax(const moeq_qweight* src, const moeq_qweight* dst, void* stream) {
   moeq_status st = check_qweight(src, MOEQ_FMT_NF4);
   if (st != MOEQ_OK) return st;
@@ -238,8 +247,40 @@ moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, co
   a.rb = route_buffers(workspace, L);
   a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
   a.y = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.y);
+  a.routed = false;
   return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream),
                                              reinterpret_cast<hipEvent_t const*>(stage_events)));
+}
+
+moeq_status moeq_experts_forward_routed(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,
+                                        int32_t K, const moeq_qweight* gu, const moeq_qweight* dn,
+                                        const int32_t* offsets, const int32_t* perm, const int32_t* slot,
+                                        uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  moeq_status st = check_forward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !idx || !wts || !out || !offsets || !perm || !slot) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const Layout L = layout((int64_t)T * K, E, I, H);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  if (!aligned16(workspace)) return MOEQ_EALIGN;
+  ForwardArgs a;
+  a.x = x; a.idx = idx; a.wts = wts;
+  a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
+  a.format = gu->format;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales; a.gu_c = gu->scale_codes;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
+  a.out = out;
+  a.rb = route_buffers(workspace, L);
+  // the caller's routing replaces the routing stage; only tile_start is derived
+  a.rb.offsets = const_cast<int32_t*>(offsets);
+  a.rb.perm = const_cast<int32_t*>(perm);
+  a.rb.slot = const_cast<int32_t*>(slot);
+  a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
+  a.y = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.y);
+  a.routed = true;
+  return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream), nullptr));
 }
 
 // Backward workspace: the routing buffers, then h bf16 [n][I], g|u fp32
@@ -311,8 +352,67 @@ moeq_status moeq_router_topk(const uint16_t* x, const uint16_t* gate, int32_t T,
   if (T == 0) return MOEQ_OK;
   if (!x || !gate || !idx || !wts) return MOEQ_EINVAL;
   if (!aligned16(x) || !aligned16(gate)) return MOEQ_EALIGN;
-  return device_status(launch_router(x, gate, T, H, E, K, renormalize ? 1 : 0, idx, wts,
+  return device_status(launch_router(x, gate, T, H, E, K, renormalize ? 1 : 0, idx, wts, nullptr, nullptr,
                                      static_cast<hipStream_t>(stream)));
+}
+
+// Router + routing workspace: chunk counts and bases [ceil(T/16)][E], the
+// per-assignment rank [T*K] and tile_start [E+1], 256-B aligned.
+struct RouterLayout {
+  size_t chunk_counts, chunk_base, rank, tile_start, total;
+};
+RouterLayout router_layout(int64_t T, int32_t K, int32_t E) {
+  RouterLayout L{};
+  const int64_t nchunk = (T + kRouterChunkTokens - 1) / kRouterChunkTokens;
+  size_t o = 0;
+  L.chunk_counts = o; o += up(sizeof(int32_t) * (size_t)(nchunk * E));
+  L.chunk_base = o;   o += up(sizeof(int32_t) * (size_t)(nchunk * E));
+  L.rank = o;         o += up(sizeof(int32_t) * (size_t)(T * K));
+  L.tile_start = o;   o += up(sizeof(int32_t) * (size_t)(E + 1));
+  L.total = o;
+  return L;
+}
+
+moeq_status check_router_route(int32_t T, int32_t H, int32_t E, int32_t K) {
+  if (T < 0 || H <= 0 || E <= 0 || K < 1) return MOEQ_EINVAL;
+  if (H % 64 != 0 || K > E || E > MOEQ_MAX_EXPERTS || K > kRouterRankMaxK) return MOEQ_ESHAPE;
+  if ((int64_t)T * H * 2 >= (int64_t(1) << 40) || (int64_t)T * K > kMaxAssignments) return MOEQ_ESHAPE;
+  return MOEQ_OK;
+}
+
+size_t moeq_router_route_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K) {
+  if (check_router_route(T, H, E, K) != MOEQ_OK) return 0;
+  return router_layout(T, K, E).total;
+}
+
+moeq_status moeq_router_route(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
+                              int32_t renormalize, int32_t* idx, float* wts, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* slot, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  moeq_status st = check_router_route(T, H, E, K);
+  if (st != MOEQ_OK) return st;
+  if (!counts || !offsets) return MOEQ_EINVAL;
+  if (T > 0 && (!x || !gate || !idx || !wts || !perm || !slot)) return MOEQ_EINVAL;
+  if (T > 0 && (!aligned16(x) || !aligned16(gate))) return MOEQ_EALIGN;
+  const RouterLayout L = router_layout(T, K, E);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  RouteBuffers rb;
+  rb.chunk_counts = reinterpret_cast<int32_t*>(w + L.chunk_counts);
+  rb.chunk_base = reinterpret_cast<int32_t*>(w + L.chunk_base);
+  rb.rank = reinterpret_cast<int32_t*>(w + L.rank);
+  rb.tile_start = reinterpret_cast<int32_t*>(w + L.tile_start);
+  rb.counts = counts;
+  rb.offsets = offsets;
+  rb.perm = perm;
+  rb.slot = slot;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (T > 0)
+    e = launch_router(x, gate, T, H, E, K, renormalize ? 1 : 0, idx, wts, rb.rank, rb.chunk_counts, s);
+  if (e == hipSuccess)
+    e = launch_route_tail(idx, T * K, E, forward_tile_rows(), kRouterChunkTokens * K, rb, s);
+  return device_status(e);
 }
 
 moeq_status moeq_qweight_copy_async(const moeq_qweight* src, const moeq_qweight* dst, void* stream) {

@@ -1737,7 +1737,8 @@ hipError_t launch_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* 
 template <int FMT>
 hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   const int32_t n = a.T * a.K;
-  hipError_t err = launch_route(a.idx, n, a.E, kBM, a.rb, s);
+  hipError_t err = a.routed ? launch_tile_start(a.rb.offsets, a.E, kBM, a.rb.tile_start, s)
+                            : launch_route(a.idx, n, a.E, kBM, a.rb, s);
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
   // upper bound on the number of token tiles: sum_e ceil(count_e / kBM)

@@ -58,6 +58,7 @@ constexpr int kNf4Buckets = 34;
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_nf4(const uint16_t* w, uint8_t* q, float* absmax, int64_t nblocks,
                                hipStream_t s);
+hipError_t launch_stream_reference(const uint16_t* w, uint8_t* q, float* absmax, int64_t nblocks, hipStream_t s);
 hipError_t launch_quantize_int8(const uint16_t* w, int8_t* q, float* scale, int64_t nrows,
                                 int32_t cols, hipStream_t s);
 hipError_t launch_dequantize_nf4(const uint8_t* q, const float* absmax, uint16_t* out,
@@ -87,6 +88,12 @@ constexpr int kRouteChunk = 256;
 int64_t route_chunks(int64_t n);
 hipError_t launch_route(const int32_t* idx, int32_t n, int32_t E, int32_t tile_rows,
                         const RouteBuffers& b, hipStream_t s);
+// Steps 2 and 3 of the routing stage (per-expert scan, scatter) over chunks of
+// `chunk` assignments whose rank and chunk_counts are already in b.
+hipError_t launch_route_tail(const int32_t* idx, int32_t n, int32_t E, int32_t tile_rows, int32_t chunk,
+                             const RouteBuffers& b, hipStream_t s);
+hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t tile_rows, int32_t* tile_start,
+                             hipStream_t s);
 
 struct ForwardArgs {
   const uint16_t* x;        // [T][H]
@@ -104,6 +111,8 @@ struct ForwardArgs {
   RouteBuffers rb;
   uint16_t* h;              // [T*K][I] bf16, expert-sorted rows
   float* y;                 // [T*K][H]: bf16 expert-sorted rows (tiled path) or fp32 (few-assignment path)
+  bool routed;              // rb.offsets / perm / slot already hold the routing of idx (only
+                            // tile_start is derived here)
 };
 // events: NULL or 5 events recorded at the stage boundaries.
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
@@ -131,8 +140,13 @@ struct BackwardArgs {
 };
 hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s);
 
+// rank / chunk_counts: nullptr, or the routing stage's rank and chunk counts
+// for chunks of kRouterChunkTokens tokens (K <= kRouterRankMaxK).
+constexpr int kRouterChunkTokens = 16;
+constexpr int kRouterRankMaxK = 64;
 hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
-                         int32_t renorm, int32_t* idx, float* wts, hipStream_t s);
+                         int32_t renorm, int32_t* idx, float* wts, int32_t* rank, int32_t* chunk_counts,
+                         hipStream_t s);
 int32_t forward_tile_rows();
 
 }  // namespace moeq

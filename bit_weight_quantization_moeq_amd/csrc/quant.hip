@@ -166,6 +166,41 @@ __global__ __launch_bounds__(kThreads) void nf4_quantize_kernel(const uint4* __r
   }
 }
 
+// Streaming reference: the launch shape, loads and stores of
+// nf4_quantize_kernel (the same 16-byte nontemporal loads of a 64-block by 8
+// lanes, 4 steps in flight, 4 B of codes per lane and 4 B of absmax per
+// block) with the code decision replaced by an XOR fold.  Its rate is the
+// attainable bandwidth for the quantize kernel's byte mix (2 B read, 0.5625 B
+// written per element) and access pattern.
+__global__ __launch_bounds__(kThreads) void stream_reference_kernel(const uint4* __restrict__ w,
+                                                                   uint32_t* __restrict__ q,
+                                                                   float* __restrict__ absmax,
+                                                                   int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7, grp = lane >> 3;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  constexpr int kPerWave = 8 * kNf4Unroll;
+  for (int64_t base = wave * kPerWave; base < nblocks; base += nwaves * kPerWave) {
+    uint4 v[kNf4Unroll];
+#pragma unroll
+    for (int u = 0; u < kNf4Unroll; ++u) {
+      int64_t b = base + u * 8 + grp;
+      b = b < nblocks ? b : nblocks - 1;
+      v[u] = ld_stream16(&w[b * 8 + sub]);
+    }
+#pragma unroll
+    for (int u = 0; u < kNf4Unroll; ++u) {
+      const int64_t b = base + u * 8 + grp;
+      const uint32_t word = v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      if (b < nblocks) {
+        q[b * 8 + sub] = word;
+        if (sub == 0) absmax[b] = __uint_as_float(word & 0x3fffffffu);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Double-quantized absmax: one workgroup per group of (at most) 256
 // consecutive blocks of one expert.  Thread t owns block t of the group: the
@@ -385,6 +420,13 @@ hipError_t launch_quantize_nf4(const uint16_t* w, uint8_t* q, float* absmax, int
   const int grid = grid_for(nblocks, (kThreads / 64) * 8 * kNf4Unroll, 8192);
   nf4_quantize_kernel<<<grid, kThreads, 0, s>>>(reinterpret_cast<const uint4*>(w),
                                                  reinterpret_cast<uint32_t*>(q), absmax, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_reference(const uint16_t* w, uint8_t* q, float* absmax, int64_t nblocks, hipStream_t s) {
+  const int grid = grid_for(nblocks, (kThreads / 64) * 8 * kNf4Unroll, 8192);
+  stream_reference_kernel<<<grid, kThreads, 0, s>>>(reinterpret_cast<const uint4*>(w),
+                                                     reinterpret_cast<uint32_t*>(q), absmax, nblocks);
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 //               chunks and the expert's total.
 //   3. scatter: per chunk, offsets from the totals (recomputed in LDS), then
 //               perm[offsets[e] + chunk_base[c][e] + rank[a]] = a.
+// The router front-end can produce step 1 itself (its workgroups are the
+// chunks: 16 tokens x K assignments each) and then runs steps 2 and 3 here.
 #include "moeq_internal.h"
 
 namespace moeq {
@@ -97,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(const int32_t* __r
   if (threadIdx.x == 0) counts[e] = carry;
 }
 
+// One workgroup per chunk of `chunk` consecutive assignments.
 __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ idx, int32_t n, int32_t E, int32_t tile_rows,
+    const int32_t* __restrict__ idx, int32_t n, int32_t E, int32_t tile_rows, int32_t chunk,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ rank, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_start,
     int32_t* __restrict__ perm, int32_t* __restrict__ slot) {
@@ -144,11 +147,13 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
     }
     if (threadIdx.x == 0) tile_start[E] = total;
   }
-  const int32_t a = blockIdx.x * kThreads + threadIdx.x;
-  if (a < n) {
+  const int32_t* base = chunk_base + (int64_t)blockIdx.x * E;
+  for (int i = threadIdx.x; i < chunk; i += kThreads) {
+    const int32_t a = blockIdx.x * chunk + i;
+    if (a >= n) break;
     const int e = idx[a];
     if (e >= 0 && e < E) {
-      const int p = off[e] + chunk_base[(int64_t)blockIdx.x * E + e] + rank[a];
+      const int p = off[e] + base[e] + rank[a];
       perm[p] = a;
       slot[a] = p;
     } else {
@@ -157,9 +162,41 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
   }
 }
 
+// tile_start = exclusive prefix of ceil(count_e / tile_rows) from offsets
+// (for a forward handed routing buffers made elsewhere); one workgroup.
+__global__ __launch_bounds__(kThreads) void tile_start_kernel(const int32_t* __restrict__ offsets, int32_t E,
+                                                             int32_t tile_rows, int32_t* __restrict__ tile_start) {
+  __shared__ int wsum[4];
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int x = 4 * threadIdx.x + i;
+    v[i] = (x < E) ? (offsets[x + 1] - offsets[x] + tile_rows - 1) / tile_rows : 0;
+    s += v[i];
+  }
+  int total;
+  int ex = block_exclusive_scan(s, wsum, &total);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int x = 4 * threadIdx.x + i;
+    if (x < E) tile_start[x] = ex;
+    ex += v[i];
+  }
+  if (threadIdx.x == 0) tile_start[E] = total;
+}
+
 }  // namespace
 
 int64_t route_chunks(int64_t n) { return (n + kRouteChunk - 1) / kRouteChunk; }
+
+hipError_t launch_route_tail(const int32_t* idx, int32_t n, int32_t E, int32_t tile_rows, int32_t chunk,
+                             const RouteBuffers& b, hipStream_t s) {
+  const int nchunk = n > 0 ? (n + chunk - 1) / chunk : 0;
+  route_scan_kernel<<<E, kThreads, 0, s>>>(b.chunk_counts, nchunk, E, b.chunk_base, b.counts);
+  route_scatter_kernel<<<nchunk > 0 ? nchunk : 1, kThreads, 0, s>>>(
+      idx, n, E, tile_rows, chunk, b.counts, b.chunk_base, b.rank, b.offsets, b.tile_start, b.perm, b.slot);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const int32_t* idx, int32_t n, int32_t E, int32_t tile_rows,
                         const RouteBuffers& b, hipStream_t s) {
@@ -167,9 +204,12 @@ hipError_t launch_route(const int32_t* idx, int32_t n, int32_t E, int32_t tile_r
   if (nchunk > 0) {
     route_rank_kernel<<<nchunk, kThreads, 0, s>>>(idx, n, E, b.chunk_counts, b.rank);
   }
-  route_scan_kernel<<<E, kThreads, 0, s>>>(b.chunk_counts, nchunk, E, b.chunk_base, b.counts);
-  route_scatter_kernel<<<nchunk > 0 ? nchunk : 1, kThreads, 0, s>>>(
-      idx, n, E, tile_rows, b.counts, b.chunk_base, b.rank, b.offsets, b.tile_start, b.perm, b.slot);
+  return launch_route_tail(idx, n, E, tile_rows, kRouteChunk, b, s);
+}
+
+hipError_t launch_tile_start(const int32_t* offsets, int32_t E, int32_t tile_rows, int32_t* tile_start,
+                             hipStream_t s) {
+  tile_start_kernel<<<1, kThreads, 0, s>>>(offsets, E, tile_rows, tile_start);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kTok = 16;  // tokens per workgroup
+constexpr int kTok = kRouterChunkTokens;  // tokens per workgroup
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -81,10 +81,12 @@ __device__ __forceinline__ float unord(uint32_t u) {
 
 // Softmax over the E logits of each of the block's tokens and the K rounds of
 // arg-max, from the logits in LDS; NPL logits per lane (E <= 64 NPL).
+// sel (LDS, or nullptr): the selections again, sel[tt * K + k] for the
+// block's token tt.
 template <int NPL>
 __device__ __forceinline__ void softmax_topk(const float* slog, int64_t t0, int32_t T, int32_t E, int32_t K,
                                              int32_t renorm, int wave, int lane, int32_t* __restrict__ idx,
-                                             float* __restrict__ wts) {
+                                             float* __restrict__ wts, int* sel) {
   // softmax and top-K: wave w takes tokens w, w + 4, w + 8, w + 12, all four
   // at once (their cross-lane reductions are independent, so their shuffle
   // latencies overlap)
@@ -151,6 +153,7 @@ __device__ __forceinline__ void softmax_topk(const float* slog, int64_t t0, int3
         } else if (lane == 0 && tok < T) {
           idx[tok * K + k] = bi;
           wts[tok * K + k] = ex * (inv[q] / sel_sum[q]);
+          if (sel) sel[(wave + kWaves * q) * K + k] = bi;
         }
       }
     }
@@ -161,12 +164,62 @@ __device__ __forceinline__ void softmax_topk(const float* slog, int64_t t0, int3
   }
 }
 
+// The chunk of this workgroup's selections (its tokens' K assignments, in
+// assignment order), ranked for the routing stage: rank[a] = the number of
+// earlier assignments of the chunk with the same expert, chunk_counts[c][e] =
+// the chunk's assignments of expert e.  The same quantities, in the same
+// order, as the routing stage's own rank step computes from top_k_index.
+// Resolves one distinct expert per wave ballot, 256 assignments at a time,
+// with running per-expert counts in LDS.  wcnt: LDS [4][E] + run [E].
+__device__ __forceinline__ void chunk_rank(const int* sel, int m, int32_t E, int* wcnt, int64_t a0,
+                                           int32_t* __restrict__ rank, int32_t* __restrict__ counts_out) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int* run = wcnt + 4 * E;
+  for (int i = t; i < 5 * E; i += kThreads) wcnt[i] = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < m; g0 += kThreads) {
+    const int j = g0 + t;
+    const bool valid = j < m;
+    const int e = valid ? sel[j] : -1;
+    int r = 0;
+    uint64_t pending = __ballot(valid);
+    while (pending) {
+      const int leader = __builtin_ctzll(pending);
+      const int el = __shfl(e, leader, 64);
+      const uint64_t same = __ballot(valid && e == el);
+      if (valid && e == el) r = __popcll(same & ((1ull << lane) - 1ull));
+      if (lane == leader) wcnt[wave * E + el] = __popcll(same);
+      pending &= ~same;
+    }
+    __syncthreads();
+    if (valid) {
+      int before = run[e];
+      for (int w = 0; w < wave; ++w) before += wcnt[w * E + e];
+      rank[a0 + j] = before + r;
+    }
+    __syncthreads();
+    for (int x = t; x < E; x += kThreads) {
+      run[x] += wcnt[x] + wcnt[E + x] + wcnt[2 * E + x] + wcnt[3 * E + x];
+      wcnt[x] = wcnt[E + x] = wcnt[2 * E + x] = wcnt[3 * E + x] = 0;
+    }
+    __syncthreads();
+  }
+  for (int x = t; x < E; x += kThreads) counts_out[x] = run[x];
+}
+
+constexpr int kMaxSel = kTok * kRouterRankMaxK;  // assignments per workgroup when ranking
+
+// rank / chunk_counts: nullptr, or the routing stage's rank [T*K] and
+// chunk_counts [ceil(T/16)][E] (chunks of 16 tokens x K assignments).
 template <int RBW>  // expert blocks of 32 per wave
 __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ gate, int32_t T, int32_t H,
                                                          int32_t E, int32_t K, int32_t renorm, int32_t P,
-                                                         int32_t* __restrict__ idx, float* __restrict__ wts) {
+                                                         int32_t* __restrict__ idx, float* __restrict__ wts,
+                                                         int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ chunk_counts) {
   extern __shared__ float slog[];  // [P][kTok][E]: partial logits of the P parts of H
+  __shared__ int sel[kMaxSel];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
@@ -249,23 +302,32 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     __syncthreads();
   }
 
+  int* sl = rank ? sel : nullptr;
   switch ((E + 63) / 64) {
-    case 1: softmax_topk<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
-    case 2: softmax_topk<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 1: softmax_topk<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 2: softmax_topk<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
     case 3:
-    case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
     case 5:
     case 6:
     case 7:
-    case 8: softmax_topk<8>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
-    default: softmax_topk<(MOEQ_MAX_EXPERTS + 63) / 64>(slog, t0, T, E, K, renorm, wave, lane, idx, wts); break;
+    case 8: softmax_topk<8>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    default: softmax_topk<(MOEQ_MAX_EXPERTS + 63) / 64>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+  }
+  if (rank) {
+    // the logits are no longer needed: their LDS holds the rank counters
+    // (4 E + E ints <= kTok E floats)
+    __syncthreads();
+    const int ntok = (int)min<int64_t>(kTok, T - t0);
+    chunk_rank(sel, ntok * K, E, reinterpret_cast<int*>(slog), t0 * K, rank, chunk_counts + (int64_t)blockIdx.x * E);
   }
 }
 
 }  // namespace
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int32_t H, int32_t E, int32_t K,
-                         int32_t renorm, int32_t* idx, float* wts, hipStream_t s) {
+                         int32_t renorm, int32_t* idx, float* wts, int32_t* rank, int32_t* chunk_counts,
+                         hipStream_t s) {
   const int grid = (T + kTok - 1) / kTok;
   const int nrb = (E + 31) / 32;  // expert blocks of 32
   // few expert blocks: split H across the waves instead (P parts, H % 64P == 0)
@@ -274,13 +336,13 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int
   const int rbw = (nrb * P + kWaves - 1) / kWaves;  // expert blocks per wave
   const size_t lds = sizeof(float) * kTok * (size_t)E * P;
   if (rbw <= 1)
-    router_kernel<1><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
+    router_kernel<1><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts, rank, chunk_counts);
   else if (rbw <= 2)
-    router_kernel<2><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
+    router_kernel<2><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts, rank, chunk_counts);
   else if (rbw <= 4)
-    router_kernel<4><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
+    router_kernel<4><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts, rank, chunk_counts);
   else
-    router_kernel<8><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts);
+    router_kernel<8><<<grid, kThreads, lds, s>>>(x, gate, T, H, E, K, renorm, P, idx, wts, rank, chunk_counts);
   return hipGetLastError();
 }
 

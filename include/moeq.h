@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define MOEQ_ABI_VERSION 2
+#define MOEQ_ABI_VERSION 3
 #define MOEQ_NF4_BLOCKSIZE 64
 #define MOEQ_DQ_GROUP 256 /* NF4 blocks per double-quantization group */
 #define MOEQ_MAX_EXPERTS 1024
@@ -125,6 +125,17 @@ moeq_status moeq_nf4_codebook(float *out);
  * Preconditions not checked on device: finite weights.
  */
 moeq_status moeq_quantize_nf4(const uint16_t *w_bf16, const moeq_qweight *dst, void *stream);
+
+/*
+ * Measurement reference, not part of the method: the launch shape, loads and
+ * stores of moeq_quantize_nf4 on a plain NF4 tensor (every bf16 element read
+ * once with the same 16-byte loads, 0.5 B of codes and 4/64 B of absmax
+ * written per element) with the NF4 decision replaced by an XOR fold, so its
+ * rate is the bandwidth attainable with the quantize kernel's byte mix and
+ * access pattern.  Same arguments and checks as moeq_quantize_nf4 (format
+ * MOEQ_FMT_NF4 only); the bytes it writes into dst are meaningless.
+ */
+moeq_status moeq_stream_reference(const uint16_t *w_bf16, const moeq_qweight *dst, void *stream);
 
 /*
  * Quantize-on-load, 8-bit ("MoE Expert Quantization", Implementation
@@ -258,6 +269,46 @@ moeq_status moeq_experts_backward(const uint16_t *hidden_bf16, const int32_t *to
 moeq_status moeq_router_topk(const uint16_t *hidden_bf16, const uint16_t *gate_bf16, int32_t T, int32_t H,
                              int32_t E, int32_t K, int32_t renormalize, int32_t *top_k_index,
                              float *top_k_weights, void *stream);
+
+/*
+ * Router front-end fused with the routing stage: the same logits, top-K and
+ * weights as moeq_router_topk, and from the same selections the grouping of
+ * the T*K assignments a = t*K + k by expert that moeq_route_buckets computes
+ * (unsloth-zoo issue #850, Suggested fix: one generic routing behind the
+ * uniform (hidden_states, top_k_index, top_k_weights) interface; "MoE Expert
+ * Quantization", Axolotl docs, Expert LoRA targeting: the router
+ * mlp.gate.weight beside the quantized experts).  The router's workgroups
+ * rank their own selections (stable, by assignment order) as they make them,
+ * so top_k_index is not read back; a per-expert scan and a scatter follow.
+ *   top_k_index, top_k_weights  as for moeq_router_topk ([T][K])
+ *   counts  int32 [E], offsets int32 [E+1], perm int32 [T*K], slot int32 [T*K]:
+ *           as for moeq_route_buckets (every selection is routed, so perm is
+ *           a full permutation and no slot is -1)
+ *   workspace  device memory of moeq_router_route_workspace_bytes(T, H, E, K)
+ * Bit-identical to moeq_router_topk followed by moeq_route_buckets.
+ * MOEQ_ESHAPE unless H % 64 == 0, 1 <= K <= min(E, 64), E <= MOEQ_MAX_EXPERTS
+ * and T*K <= 2^24; T == 0 writes zero counts and offsets.
+ */
+size_t moeq_router_route_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K);
+moeq_status moeq_router_route(const uint16_t *hidden_bf16, const uint16_t *gate_bf16, int32_t T, int32_t H,
+                              int32_t E, int32_t K, int32_t renormalize, int32_t *top_k_index,
+                              float *top_k_weights, int32_t *counts, int32_t *offsets, int32_t *perm,
+                              int32_t *slot, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moeq_experts_forward with the routing already done: offsets, perm and slot
+ * are the grouping of this top_k_index by expert (as moeq_router_route or
+ * moeq_route_buckets wrote it), so the routing stage is skipped.  Same
+ * arguments, workspace, rules and results as moeq_experts_forward (the
+ * output is bit-identical).  Preconditions not checked on device: the
+ * routing buffers belong to this top_k_index.
+ */
+moeq_status moeq_experts_forward_routed(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                        const float *top_k_weights, int32_t T, int32_t K,
+                                        const moeq_qweight *gate_up, const moeq_qweight *down,
+                                        const int32_t *offsets, const int32_t *perm, const int32_t *slot,
+                                        uint16_t *out_bf16, void *workspace, size_t workspace_bytes,
+                                        void *stream);
 
 /*
  * Asynchronous copy of one packed expert tensor (codes and scales) between

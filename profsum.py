@@ -6,6 +6,8 @@
         <algorithmic_bytes> "<fetch command>" "<write command>"
     python profsum.py decode <kernel_trace.csv> <H> <I> \
         <format>=<bytes_per_weight>[,...] <grid_x>=<touched experts>[,...] "<command>"
+    python profsum.py counters <pmc_dir> <kernel>[@<workload>] <simd_count> \
+        <algorithmic_flops> "<command>"
 
 ``stats`` prints a per-kernel duration table.  ``traffic`` reads two
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch), takes the
@@ -16,6 +18,16 @@ block that bench.py reads; the block carries the SHA-256 of the kernel
 sources so that a changed kernel reports no stale traffic.  ``decode`` splits
 the few-assignment kernels' dispatches by launch grid (one grid per batch
 size) and prices each against the packed bytes of the experts it touches.
+``counters`` averages every counter of one ``--pmc`` run per dispatch of
+``kernel`` and derives the MFMA busy fraction (the summed per-SIMD
+SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD count, the
+definition rocprofv3 gives MfmaUtil) and the flops the MFMA op counter implies
+(SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 flops).
+
+A kernel argument may carry ``@<workload>`` (e.g. ``g1_kernel<1>@mixtral_T16384``):
+the tag names the workload in the JSON block, which bench.py matches against
+the configuration it measures; the counters are read for the bare kernel
+name, so the profiled command must run that kernel on that workload only.
 """
 
 import csv
@@ -39,13 +51,30 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-def source_hash():
-    """SHA-256 of the kernel sources' code (comments and layout ignored)."""
+def _kernel_file(kernel):
+    """The source under csrc/ that defines `kernel` (bare name, template
+    arguments and any @workload tag dropped), or None."""
     here = os.path.dirname(os.path.abspath(__file__))
-    h = hashlib.sha256()
+    base = kernel.split("@", 1)[0].split("<", 1)[0].strip()
     for rel in SOURCES:
-        with open(os.path.join(here, rel)) as f:
-            h.update(_code_only(f.read()).encode())
+        if rel.endswith(".hip"):
+            with open(os.path.join(here, rel)) as f:
+                if re.search(r"__global__[^;{]*\b" + re.escape(base) + r"\s*\(", f.read()):
+                    return rel
+    return None
+
+
+def source_hash(kernel=None):
+    """SHA-256 of the kernel sources' code (comments and layout ignored): of
+    the file that defines `kernel` plus the shared internal header, or of
+    every source when no kernel is named (or its file is not found)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    f = _kernel_file(kernel) if kernel else None
+    files = (f, f"{PKG}/csrc/moeq_internal.h") if f else SOURCES
+    h = hashlib.sha256()
+    for rel in files:
+        with open(os.path.join(here, rel)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -88,23 +117,68 @@ def _per_dispatch(d, counter):
     return out
 
 
+def _bare(kernel):
+    return kernel.split("@", 1)[0]
+
+
 def traffic(fetch_dir, write_dir, kernel, copy_bytes, algo_bytes, cmd_f, cmd_w):
     copy_bytes, algo_bytes = float(copy_bytes), float(algo_bytes)
+    k = _bare(kernel)
     f, w = _per_dispatch(fetch_dir, "FETCH_SIZE"), _per_dispatch(write_dir, "WRITE_SIZE")
     cf = max(f["__amd_rocclr_copyBuffer"]) * 1024.0 / copy_bytes   # counter bytes per copied byte
     cw = max(w["__amd_rocclr_copyBuffer"]) * 1024.0 / copy_bytes
-    fk = sum(f[kernel]) / len(f[kernel]) * 1024.0 / cf
-    wk = sum(w[kernel]) / len(w[kernel]) * 1024.0 / cw
+    fk = sum(f[k]) / len(f[k]) * 1024.0 / cf
+    wk = sum(w[k]) / len(w[k]) * 1024.0 / cw
     print(f"FETCH_SIZE command: `{cmd_f}`\n\nWRITE_SIZE command: `{cmd_w}`\n")
     print(f"Calibration: the largest `__amd_rocclr_copyBuffer` dispatch copies {copy_bytes:.0f} bytes; "
           f"FETCH_SIZE reads {cf:.3f} and WRITE_SIZE {cw:.3f} counter bytes per copied byte.\n")
     print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB (cal.) | HBM write MB (cal.) "
           "| algorithmic MB | traffic / algorithmic |")
     print("|---|---:|---:|---:|---:|---:|---:|---:|")
-    print(f"| {kernel} | {len(f[kernel])} | {sum(f[kernel]) / len(f[kernel]):.0f} | {sum(w[kernel]) / len(w[kernel]):.0f} "
+    print(f"| {k} | {len(f[k])} | {sum(f[k]) / len(f[k]):.0f} | {sum(w[k]) / len(w[k]):.0f} "
           f"| {fk / 1e6:.1f} | {wk / 1e6:.1f} | {algo_bytes / 1e6:.1f} | {(fk + wk) / algo_bytes:.3f} |")
     block = {"kernel": kernel, "hbm_read_bytes": fk, "hbm_write_bytes": wk, "traffic_bytes": fk + wk,
-             "algorithmic_bytes": algo_bytes, "source_sha256": source_hash()}
+             "algorithmic_bytes": algo_bytes, "source_sha256": source_hash(kernel)}
+    print("\n```json\n" + json.dumps(block) + "\n```")
+
+
+def _all_counters(d):
+    """kernel short name -> list of {counter: value} per dispatch."""
+    out = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        acc = {}
+        for r in csv.DictReader(open(p)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            c = acc.setdefault(key, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for (_, name), c in acc.items():
+            out.setdefault(short(name), []).append(c)
+    return out
+
+
+def counters(pmc_dir, kernel, simds, algo_flops, command):
+    simds, algo_flops = int(simds), float(algo_flops)
+    k = _bare(kernel)
+    per = _all_counters(pmc_dir)[k]
+    names = sorted({n for c in per for n in c})
+    mean = {n: sum(c.get(n, 0.0) for c in per) / len(per) for n in names}
+    print(f"command: `{command}`\n")
+    print(f"{len(per)} dispatches of `{k}`; mean per dispatch:\n")
+    print("| counter | mean per dispatch |")
+    print("|---|---:|")
+    for n in names:
+        print(f"| {n} | {mean[n]:.6g} |")
+    block = {"kernel": kernel, "dispatches": len(per), "counters": mean, "source_sha256": source_hash(kernel)}
+    if "MfmaUtil" in mean:
+        block["mfma_util"] = mean["MfmaUtil"] / 100.0
+        print(f"\nMFMA busy (rocprofv3's MfmaUtil: the summed per-SIMD SQ_VALU_MFMA_BUSY_CYCLES over the "
+              f"largest GRBM_GUI_ACTIVE instance times the SIMD count): {mean['MfmaUtil']:.1f} % "
+              f"(mean over dispatches).")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean and algo_flops > 0:
+        block["counter_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        block["algorithmic_flops"] = algo_flops
+        print(f"\nbf16 MFMA flops from the op counter (x 512): {block['counter_flops']:.4g} per dispatch, "
+              f"against {algo_flops:.4g} algorithmic ({block['counter_flops'] / algo_flops:.3f} x).")
     print("\n```json\n" + json.dumps(block) + "\n```")
 
 
@@ -148,5 +222,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:9])
     elif sys.argv[1] == "decode":
         decode(*sys.argv[2:8])
+    elif sys.argv[1] == "counters":
+        counters(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)

@@ -35,7 +35,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert moeq.moeq_abi_version() == 2
+    assert moeq.moeq_abi_version() == 3
     m = re.search(r"#define\s+MOEQ_ABI_VERSION\s+(\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == moeq.ABI_VERSION == moeq.moeq_abi_version()
     for s in range(0, -8, -1):
