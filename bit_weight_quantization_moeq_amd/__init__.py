@@ -23,6 +23,7 @@ __all__ = [
     "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
     "moeq_qweight_copy_async", "FMT_NF4_DQ", "DQ_GROUP", "moeq_compress_absmax",
     "moeq_stream_reference", "moeq_router_route", "moeq_experts_forward_routed", "Routing",
+    "moeq_experts_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 FMT_NF4 = 1
@@ -31,6 +32,7 @@ FMT_NF4_DQ = 3
 NF4_BLOCKSIZE = 64
 DQ_GROUP = 256
 ABI_VERSION = 3
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libmoeq.so")
@@ -85,6 +87,7 @@ def _load():
         "moeq_router_route_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "moeq_router_route": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P]),
         "moeq_experts_forward_routed": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, P, SZ, P]),
+        "moeq_experts_forward_noalloc": (I32, [P, P, P, I32, I32, QP, QP, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -431,6 +434,24 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
             raise ValueError("stage_events must hold 5 hipEvent_t handles")
         arr = (ctypes.c_void_p * 5)(*[int(e) for e in stage_events])
         _check(lib.moeq_experts_forward_timed(*args, arr), "moeq_experts_forward_timed")
+    return out
+
+
+def moeq_experts_forward_noalloc(hidden, top_k_index, top_k_weights, gate_up, down, out, stream=None):
+    """:func:`moeq_experts_forward` into the caller's ``out`` (bf16 ``[T, H]``)
+    with the library's own device scratch as workspace: the library call
+    allocates nothing (for callers that cannot allocate, e.g. under graph
+    capture).  Raises :class:`MoeqError` (workspace status) when the batch
+    needs more than ``NOALLOC_SCRATCH_BYTES``.  Calls overlapping in time on
+    one GPU share that scratch and must be serialised by the caller."""
+    T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
+    _dev(out, torch.bfloat16, "out", (T, H))
+    wt = _forward_weights(gate_up, down, H)
+    _on_device("moeq_experts_forward_noalloc", hidden, top_k_index, top_k_weights, out, *wt)
+    gu, dn = gate_up._c(), down._c()
+    _check(_load().moeq_experts_forward_noalloc(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T),
+                                                int(K), ctypes.byref(gu), ctypes.byref(dn), _ptr(out),
+                                                _stream(stream)), "moeq_experts_forward_noalloc")
     return out
 
 

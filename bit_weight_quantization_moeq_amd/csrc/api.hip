@@ -5,6 +5,8 @@
 // #1849 and unsloth-zoo issue #850 are what these checks exist to prevent).
 #include <string.h>
 
+#include <mutex>
+
 #include "moeq_internal.h"
 
 using namespace moeq;
@@ -99,6 +101,34 @@ RouteBuffers route_buffers(void* ws, const Layout& L) {
 }
 
 constexpr int64_t kMaxAssignments = int64_t(1) << 24;
+
+// Device-resident scratch for moeq_experts_forward_noalloc: the forward's
+// workspace for callers that cannot allocate.  Each GPU the library runs on
+// holds its own copy for the life of the process.  Host code never uses the
+// array's name as an address (on the host it is only a handle): the device
+// address comes from hipGetSymbolAddress, once per device with that device
+// current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[MOEQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The scratch address on the current device (resolved on the first call there).
+hipError_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 moeq_status check_forward_shapes(int32_t T, int32_t K, const moeq_qweight* gu, const moeq_qweight* dn) {
   if (T < 0 || K < 1) return MOEQ_EINVAL;
@@ -250,6 +280,23 @@ moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, co
   a.routed = false;
   return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream),
                                              reinterpret_cast<hipEvent_t const*>(stage_events)));
+}
+
+moeq_status moeq_experts_forward_noalloc(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,
+                                         int32_t K, const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
+                                         void* stream) {
+  moeq_status st = check_forward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !idx || !wts || !out) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const Layout L = layout((int64_t)T * K, E, I, H);
+  if (L.total > (size_t)MOEQ_NOALLOC_SCRATCH_BYTES) return MOEQ_EWORKSPACE;
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess || !ws) return MOEQ_EDEVICE;
+  return moeq_experts_forward_timed(x, idx, wts, T, K, gu, dn, out, ws, MOEQ_NOALLOC_SCRATCH_BYTES, stream,
+                                    nullptr);
 }
 
 moeq_status moeq_experts_forward_routed(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,

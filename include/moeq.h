@@ -220,6 +220,30 @@ moeq_status moeq_experts_forward_timed(const uint16_t *hidden_bf16, const int32_
                                        void *stream, void *const *stage_events);
 
 /*
+ * moeq_experts_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and results, without the
+ * workspace argument.  The workspace is a device array inside the library of
+ * MOEQ_NOALLOC_SCRATCH_BYTES (64 MiB), which each GPU the library runs on
+ * holds until the process ends; its address on the current device is looked
+ * up on the first call there (the stream must belong to the current device).
+ * The call allocates nothing.  MOEQ_EWORKSPACE when
+ * moeq_experts_forward_workspace_bytes(T, K, gate_up, down) exceeds the array
+ * (the largest batches that fit: 818 tokens of an OLMoE-shaped layer at
+ * top-8, 744 of a Mixtral-shaped one at top-2; every few-assignment batch
+ * fits).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different
+ * streams, or threads) race and must be serialised by the caller.  Nothing
+ * in the array needs clearing between calls (every byte the forward reads is
+ * written earlier in the same call).
+ */
+#define MOEQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+moeq_status moeq_experts_forward_noalloc(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                         const float *top_k_weights, int32_t T, int32_t K,
+                                         const moeq_qweight *gate_up, const moeq_qweight *down,
+                                         uint16_t *out_bf16, void *stream);
+
+/*
  * Gradients of the routed experts block with respect to its inputs, the
  * packed weights frozen: the workload the quantized experts serve is adapter
  * training over frozen 4-bit/8-bit experts ("MoE Expert Quantization",

@@ -135,6 +135,10 @@ int main() {
   EXPECT(moeq_router_route(x, x, T, H, E, K, 0, idx, wts, nullptr, idx, idx, idx, ws, need, nullptr), MOEQ_EINVAL);
   EXPECT(moeq_route_buckets(idx, T, K, E, nullptr, idx, idx, idx, ws, need, nullptr), MOEQ_EINVAL);
   EXPECT(moeq_route_buckets(idx, T, K, 0, idx, idx, idx, idx, ws, need, nullptr), MOEQ_EINVAL);
+  EXPECT(moeq_experts_forward_noalloc(x, idx, wts, T, 0, &gu, &dn, out, nullptr), MOEQ_EINVAL);
+  EXPECT(moeq_experts_forward_noalloc(x, idx, wts, 0, K, &gu, &dn, nullptr, nullptr), MOEQ_OK);
+  EXPECT(moeq_experts_forward_noalloc(nullptr, idx, wts, T, K, &gu, &dn, out, nullptr), MOEQ_EINVAL);
+  EXPECT(moeq_experts_forward_noalloc(x, idx, wts, 1 << 20, K, &gu, &dn, out, nullptr), MOEQ_EWORKSPACE);
   if (g_launches != 0) { fprintf(stderr, "a rejected call launched work (%d)\n", g_launches); ++failures; }
 
   // calls that pass validation reach exactly their launchers (stubs here)
