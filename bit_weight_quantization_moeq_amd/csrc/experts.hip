@@ -52,7 +52,10 @@
 //     natural k order within each group of 8.
 //   * Work items (expert, column tile, token tile) are laid out expert-major
 //     and dealt to the 8 XCDs in contiguous ranges, so the tiles that share an
-//     expert's weights and token rows run on the same L2.
+//     expert's weights and token rows run on the same L2; within an expert the
+//     token tiles go in groups of four, column tile by column tile, so the
+//     items in flight on one XCD share four token tiles and a few weight
+//     column tiles instead of re-reading every token tile per column tile.
 #include <type_traits>
 
 #include "moeq_internal.h"
@@ -457,10 +460,12 @@ struct FragStages<MOEQ_FMT_INT8_ROWWISE> {
 };
 
 // ---------------------------------------------------------------------------
-// Work items: expert-major (expert, column tile, token tile), dealt to the
-// XCDs in contiguous ranges.  tile_start = exclusive prefix of per-expert
-// token-tile counts.
+// Work items: expert-major (expert, group of kTileGroup token tiles, column
+// tile, token tile within the group), dealt to the XCDs in contiguous
+// ranges.  tile_start = exclusive prefix of per-expert token-tile counts.
 // ---------------------------------------------------------------------------
+constexpr int kTileGroup = 4;
+
 // Rows [*row0, *row0 + *nrows) of tile mt of expert e: the expert's rows
 // split into tile_start[e+1] - tile_start[e] near-equal tiles (at most kBM
 // rows each, since the count is ceil(rows / kBM)).
@@ -488,8 +493,15 @@ __device__ __forceinline__ bool decode_work(const int32_t* tile_start, int E, in
   e = lo;
   const int r = w - tile_start[e] * ncol;
   const int nt = tile_start[e + 1] - tile_start[e];
-  ct = r / nt;
-  mt = r - ct * nt;
+  // the expert's token tiles in groups of kTileGroup; a group's items run
+  // column tile by column tile, so the items in flight on an XCD at once
+  // share a few token tiles and a few weight column tiles, each K step of
+  // which is fetched once into that XCD's L2
+  const int g = r / (kTileGroup * ncol);
+  const int gt = min(kTileGroup, nt - g * kTileGroup);
+  const int rr = r - g * kTileGroup * ncol;
+  ct = rr / gt;
+  mt = g * kTileGroup + (rr - ct * gt);
   return true;
 }
 

@@ -6,7 +6,7 @@
         <algorithmic_bytes> "<fetch command>" "<write command>"
     python profsum.py decode <kernel_trace.csv> <H> <I> \
         <format>=<bytes_per_weight>[,...] <grid_x>=<touched experts>[,...] "<command>"
-    python profsum.py counters <pmc_dir> <kernel>[@<workload>] <simd_count> \
+    python profsum.py counters <pmc_dir> <kernel>[@<workload>] <simd_count|0> \
         <algorithmic_flops> "<command>"
 
 ``stats`` prints a per-kernel duration table.  ``traffic`` reads two
@@ -20,9 +20,12 @@ the few-assignment kernels' dispatches by launch grid (one grid per batch
 size) and prices each against the packed bytes of the experts it touches.
 ``counters`` averages every counter of one ``--pmc`` run per dispatch of
 ``kernel`` and derives the MFMA busy fraction (the summed per-SIMD
-SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD count, the
-definition rocprofv3 gives MfmaUtil) and the flops the MFMA op counter implies
-(SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 flops).
+SQ_VALU_MFMA_BUSY_CYCLES over the GPU's busy cycles times the SIMD count, the
+definition rocprofv3 gives MfmaUtil; GRBM_GUI_ACTIVE arrives summed over the
+XCDs, so one XCD's busy cycles are that sum over the agent's Num_Xcc), the
+shader clock the busy cycles imply over the dispatch's duration, and the flops
+the MFMA op counter implies (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512
+flops).  ``simd_count`` 0 takes the SIMD count from the agent info.
 
 A kernel argument may carry ``@<workload>`` (e.g. ``g1_kernel<1>@mixtral_T16384``):
 the tag names the workload in the JSON block, which bench.py matches against
@@ -143,7 +146,8 @@ def traffic(fetch_dir, write_dir, kernel, copy_bytes, algo_bytes, cmd_f, cmd_w):
 
 
 def _all_counters(d):
-    """kernel short name -> list of {counter: value} per dispatch."""
+    """kernel short name -> list of {counter: value} per dispatch (plus the
+    dispatch's duration in ns under "duration_ns")."""
     out = {}
     for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         acc = {}
@@ -151,13 +155,26 @@ def _all_counters(d):
             key = (r["Dispatch_Id"], r["Kernel_Name"])
             c = acc.setdefault(key, {})
             c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            c["duration_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         for (_, name), c in acc.items():
             out.setdefault(short(name), []).append(c)
     return out
 
 
+def _gpu_agent(d):
+    """The GPU row of the run's agent info (Num_Xcc, Simd_Count, ...), or {}."""
+    for p in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(p)):
+            if r.get("Name", "").startswith("gfx"):
+                return r
+    return {}
+
+
 def counters(pmc_dir, kernel, simds, algo_flops, command):
-    simds, algo_flops = int(simds), float(algo_flops)
+    algo_flops = float(algo_flops)
+    agent = _gpu_agent(pmc_dir)
+    simds = int(simds) or int(agent.get("Simd_Count", 0))
+    nxcc = int(agent.get("Num_Xcc", 1) or 1)
     k = _bare(kernel)
     per = _all_counters(pmc_dir)[k]
     names = sorted({n for c in per for n in c})
@@ -174,6 +191,14 @@ def counters(pmc_dir, kernel, simds, algo_flops, command):
         print(f"\nMFMA busy (rocprofv3's MfmaUtil: the summed per-SIMD SQ_VALU_MFMA_BUSY_CYCLES over the "
               f"largest GRBM_GUI_ACTIVE instance times the SIMD count): {mean['MfmaUtil']:.1f} % "
               f"(mean over dispatches).")
+    elif "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean and simds > 0:
+        util = [c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / nxcc * simds) for c in per]
+        clk = [c["GRBM_GUI_ACTIVE"] / nxcc / c["duration_ns"] for c in per]
+        block["mfma_util"] = sum(util) / len(util)
+        block["shader_clock_GHz"] = sum(clk) / len(clk)
+        print(f"\nMFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {nxcc} XCDs x {simds} SIMDs) = "
+              f"{100 * block['mfma_util']:.1f} % of the busy cycles (mean over dispatches); those cycles over "
+              f"the dispatch duration give a shader clock of {block['shader_clock_GHz']:.3f} GHz.")
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean and algo_flops > 0:
         block["counter_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
         block["algorithmic_flops"] = algo_flops

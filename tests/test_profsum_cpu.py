@@ -89,3 +89,29 @@ def test_traffic_calibration(tmp_path, capsys):
     assert block["hbm_write_bytes"] == 64.0 * 1024
     assert block["traffic_bytes"] == block["hbm_read_bytes"] + block["hbm_write_bytes"]
     assert block["source_sha256"] == profsum.source_hash()
+
+
+def test_counters_mfma_busy_and_clock(tmp_path, capsys):
+    # 2 XCDs, 8 SIMDs: GRBM_GUI_ACTIVE arrives summed over the XCDs (2 x 1000
+    # busy cycles over a 500 ns dispatch: 2 GHz); the SIMDs were MFMA-busy for
+    # 4000 of their 8 x 1000 cycles (50 %); 10 MFMA op units of 512 flops
+    d = tmp_path / "c"
+    d.mkdir()
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for disp in (1, 2):
+        for name, v in (("GRBM_GUI_ACTIVE", 2000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 4000.0),
+                        ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 10.0)):
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": "void moeq::(anonymous namespace)::g<1>(int)",
+                         "Counter_Name": name, "Counter_Value": v, "Start_Timestamp": 1000,
+                         "End_Timestamp": 1500})
+    _write(d / "7_counter_collection.csv", cols, rows)
+    _write(d / "7_agent_info.csv", ["Name", "Num_Xcc", "Simd_Count"],
+           [{"Name": "cpu", "Num_Xcc": 0, "Simd_Count": 0}, {"Name": "gfx950", "Num_Xcc": 2, "Simd_Count": 8}])
+    profsum.counters(str(d), "g<1>@w", 0, 5120.0, "cmd")
+    out = capsys.readouterr().out
+    block = json.loads(out.split("```json\n")[1].split("\n```")[0])
+    assert block["kernel"] == "g<1>@w" and block["dispatches"] == 2
+    assert abs(block["mfma_util"] - 0.5) < 1e-12
+    assert abs(block["shader_clock_GHz"] - 2.0) < 1e-12
+    assert block["counter_flops"] == 5120.0 and block["algorithmic_flops"] == 5120.0
