@@ -8,6 +8,7 @@
         <format>=<bytes_per_weight>[,...] <grid_x>=<touched experts>[,...] "<command>"
     python profsum.py counters <pmc_dir> <kernel>[@<workload>] <simd_count|0> \
         <algorithmic_flops> "<command>"
+    python profsum.py kernels <pmc_dir> "<command>"
 
 ``stats`` prints a per-kernel duration table.  ``traffic`` reads two
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs (KiB per dispatch), takes the
@@ -26,6 +27,8 @@ XCDs, so one XCD's busy cycles are that sum over the agent's Num_Xcc), the
 shader clock the busy cycles imply over the dispatch's duration, and the flops
 the MFMA op counter implies (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512
 flops).  ``simd_count`` 0 takes the SIMD count from the agent info.
+``kernels`` prints those derived figures, and the SQ stall fractions when
+the run counted them, for every kernel of the library in one run.
 
 A kernel argument may carry ``@<workload>`` (e.g. ``g1_kernel<1>@mixtral_T16384``):
 the tag names the workload in the JSON block, which bench.py matches against
@@ -207,6 +210,51 @@ def counters(pmc_dir, kernel, simds, algo_flops, command):
     print("\n```json\n" + json.dumps(block) + "\n```")
 
 
+def kernels(pmc_dir, command, prefix="moeq::"):
+    """One row per kernel of the library (names starting with `prefix`) in a
+    --pmc run: dispatches, mean duration, and whichever derived figures its
+    counters allow -- the MFMA busy fraction and shader clock (as in
+    ``counters``) and, from the SQ stall counters, the fractions of the
+    waves' cycles spent waiting on a counter (SQ_WAIT_INST_ANY), waiting for
+    anything (SQ_WAIT_ANY), issuing VALU (SQ_ACTIVE_INST_VALU, MFMA included)
+    and LDS (SQ_ACTIVE_INST_LDS) instructions."""
+    agent = _gpu_agent(pmc_dir)
+    simds = int(agent.get("Simd_Count", 0) or 0)
+    nxcc = int(agent.get("Num_Xcc", 1) or 1)
+    per = {}
+    for p in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        acc = {}
+        for r in csv.DictReader(open(p)):
+            if not r["Kernel_Name"].replace("void ", "").startswith(prefix):
+                continue
+            c = acc.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            c["duration_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        for (_, name), c in acc.items():
+            per.setdefault(short(name), []).append(c)
+    print(f"command: `{command}`\n")
+    print("| kernel | dispatches | mean us | MFMA busy | clock GHz | wait on counter | wait any | VALU issue | LDS issue |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    rows = {}
+    for k in sorted(per, key=lambda k: -sum(c["duration_ns"] for c in per[k])):
+        cs = per[k]
+        tot = lambda n: sum(c.get(n, 0.0) for c in cs)
+        row = {"dispatches": len(cs), "mean_us": tot("duration_ns") / len(cs) / 1e3}
+        if tot("SQ_VALU_MFMA_BUSY_CYCLES") > 0 and tot("GRBM_GUI_ACTIVE") > 0 and simds:
+            row["mfma_busy"] = tot("SQ_VALU_MFMA_BUSY_CYCLES") / (tot("GRBM_GUI_ACTIVE") / nxcc * simds)
+            row["clock_GHz"] = tot("GRBM_GUI_ACTIVE") / nxcc / tot("duration_ns")
+        if tot("SQ_WAVE_CYCLES") > 0:
+            for n, key in (("SQ_WAIT_INST_ANY", "wait_counter"), ("SQ_WAIT_ANY", "wait_any"),
+                           ("SQ_ACTIVE_INST_VALU", "valu"), ("SQ_ACTIVE_INST_LDS", "lds")):
+                if n in cs[0]:
+                    row[key] = tot(n) / tot("SQ_WAVE_CYCLES")
+        f = lambda key, fmt: (fmt.format(row[key]) if key in row else "")
+        print(f"| {k} | {row['dispatches']} | {row['mean_us']:.1f} | {f('mfma_busy', '{:.1%}')} | {f('clock_GHz', '{:.2f}')} "
+              f"| {f('wait_counter', '{:.1%}')} | {f('wait_any', '{:.1%}')} | {f('valu', '{:.1%}')} | {f('lds', '{:.1%}')} |")
+        rows[k] = row
+    return rows
+
+
 def decode(trace, H, I, bpw, grids, command):
     """Per-launch-grid durations of the few-assignment kernels from a
     --kernel-trace CSV, and GB/s over the touched experts' packed weights
@@ -249,5 +297,7 @@ if __name__ == "__main__":
         decode(*sys.argv[2:8])
     elif sys.argv[1] == "counters":
         counters(*sys.argv[2:7])
+    elif sys.argv[1] == "kernels":
+        kernels(sys.argv[2], sys.argv[3])
     else:
         raise SystemExit(__doc__)

@@ -115,3 +115,31 @@ def test_counters_mfma_busy_and_clock(tmp_path, capsys):
     assert abs(block["mfma_util"] - 0.5) < 1e-12
     assert abs(block["shader_clock_GHz"] - 2.0) < 1e-12
     assert block["counter_flops"] == 5120.0 and block["algorithmic_flops"] == 5120.0
+
+
+def test_kernels_table(tmp_path, capsys):
+    # two library kernels and a foreign one; 1 XCD, 4 SIMDs
+    d = tmp_path / "k"
+    d.mkdir()
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for disp, name, ctr in ((1, "moeq::(anonymous namespace)::a_kernel(int)",
+                             {"GRBM_GUI_ACTIVE": 1000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1000.0,
+                              "SQ_WAVE_CYCLES": 200.0, "SQ_WAIT_INST_ANY": 50.0, "SQ_WAIT_ANY": 20.0,
+                              "SQ_ACTIVE_INST_VALU": 100.0, "SQ_ACTIVE_INST_LDS": 10.0}),
+                            (2, "void moeq::(anonymous namespace)::b_kernel<2>(int)", {"SQ_WAVE_CYCLES": 100.0,
+                                                                                    "SQ_WAIT_INST_ANY": 10.0}),
+                            (3, "void at::native::fill(int)", {"SQ_WAVE_CYCLES": 5.0})):
+        for n, v in ctr.items():
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": n, "Counter_Value": v,
+                         "Start_Timestamp": 0, "End_Timestamp": 2000})
+    _write(d / "1_counter_collection.csv", cols, rows)
+    _write(d / "1_agent_info.csv", ["Name", "Num_Xcc", "Simd_Count"], [{"Name": "gfx950", "Num_Xcc": 1, "Simd_Count": 4}])
+    got = profsum.kernels(str(d), "cmd")
+    capsys.readouterr()
+    assert set(got) == {"a_kernel", "b_kernel<2>"}
+    a = got["a_kernel"]
+    assert abs(a["mfma_busy"] - 0.25) < 1e-12 and abs(a["clock_GHz"] - 0.5) < 1e-12
+    assert (a["wait_counter"], a["wait_any"], a["valu"], a["lds"]) == (0.25, 0.1, 0.5, 0.05)
+    assert got["b_kernel<2>"]["wait_counter"] == 0.1 and "mfma_busy" not in got["b_kernel<2>"]
+    assert a["mean_us"] == 2.0
