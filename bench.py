@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--parts", default=",".join(PARTS),
                     help=f"comma list of records to produce (default all: {','.join(PARTS)})")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cases", default="",
+                    help="comma list of shape:T forward cases (e.g. olmoe:32) to run instead of every configured "
+                         "one, plain back-to-back calls only (for counter runs of one case)")
     return ap.parse_args()
 
 
@@ -366,19 +369,22 @@ def layer_stack(torch, moeq, syn, s, fmt, dev, per_call_bytes, target=4 * LLC_BY
     return [(qg, qd)] + [(clone_q(moeq, qg), clone_q(moeq, qd)) for _ in range(n - 1)]
 
 
-def config_records(torch, moeq, syn, dev, copy_GBps, log, decode_only=False):
+def config_records(torch, moeq, syn, dev, copy_GBps, log, decode_only=False, cases=None):
     """Every configured shape and batch size in the shape's format: the
     forward (tokens/s, TFLOP/s, GB/s over the touched experts' packed bytes);
-    few-assignment batches also as a HIP-graph replay and split per kernel."""
+    few-assignment batches also as a HIP-graph replay and split per kernel.
+    `cases`: only these (shape, T) pairs, back-to-back calls only."""
     out = []
     for name, s in syn.SHAPES.items():
         Ts = tuple(T for T in s.tokens if T * s.K <= 512) if decode_only else s.tokens
+        if cases is not None:
+            Ts = tuple(T for (n, T) in cases if n == name)
         for T in Ts:
             log(f"forward {name} T={T}")
             idx, _ = syn.routing(T, s.K, s.E, kind=s.routing, device=dev, layer=1)
             wbytes, _, _ = touched_bytes(s, idx, s.fmt)
             stack = layer_stack(torch, moeq, syn, s, s.fmt, dev, wbytes)
-            dec = T * s.K <= 512
+            dec = T * s.K <= 512 and cases is None
             out.append(forward_case(torch, moeq, syn, s, s.fmt, stack, T, dev, copy_GBps, graph=dec, stage=dec))
             del stack
             torch.cuda.empty_cache()
@@ -701,7 +707,14 @@ def main():
                   "stage_ms", "touched_experts", "forward_ms_with_stage_events"):
             result[k] = rec[k]
         torch.cuda.empty_cache()
-    if "configs" in parts or "decode" in parts:
+    if args.cases:
+        cases = [(c.split(":")[0], int(c.split(":")[1])) for c in args.cases.split(",")]
+        bad = [c for c in cases if c[0] not in syn.SHAPES]
+        if bad:
+            raise SystemExit(f"unknown shapes in --cases: {bad}; choose from {sorted(syn.SHAPES)}")
+        log(f"forward cases {cases}")
+        result["forward_configs"] = config_records(torch, moeq, syn, dev, copy_GBps, log, cases=cases)
+    elif "configs" in parts or "decode" in parts:
         log("forward at every configured shape and batch size")
         result["forward_configs"] = config_records(torch, moeq, syn, dev, copy_GBps, log,
                                                    decode_only="configs" not in parts)

@@ -1018,7 +1018,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int FMT, bool G1, int NW, bool PAIR>
+// AB: how plain-NF4 absmax reach the lanes -- 0: one load per K step and row;
+// 2: a pair per two steps (PAIR below); 8: eight per lane per eight steps
+// (OCT below).
+template <int FMT, bool G1, int NW, int AB>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restrict__ act,
                                                         const int32_t* __restrict__ idx,
                                                         const float* __restrict__ wts, int32_t n, int32_t Ktop,
@@ -1092,8 +1095,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   const uint8_t* q1 = wq + ((int64_t)e * R + r1) * cpr;
   const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, R, r0, K, 0);
   const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, R, r1, K, 0);
-  const int nks = (K + kStep - 1) / kStep, nkp = (nks + 1) / 2;  // steps, pairs of steps
-  const int ks0 = 2 * (part * nkp / P), ks1 = min(2 * ((part + 1) * nkp / P), nks);
+  // Parts are whole groups of gran K steps: eights when K is a multiple of
+  // 1024 and the P parts split the steps into equal eights (the condition
+  // under which the host picks AB = 8), else pairs.  The split depends on
+  // the shape only, not on AB, so every format sums the same parts.
+  constexpr int kTrip = AB == 8 ? 8 : 2;  // steps per loop trip
+  constexpr bool PAIR = AB == 2;
+  const int nks = (K + kStep - 1) / kStep;
+  const int gran = (K % 1024 == 0 && nks % (8 * P) == 0) ? 8 : 2;
+  const int nkp = (nks + gran - 1) / gran;  // groups of steps
+  const int ks0 = gran * (part * nkp / P), ks1 = min(gran * ((part + 1) * nkp / P), nks);
   // int8: the row scales, first of this wave's loads
   float rs0 = 0.0f, rs1 = 0.0f;
   if constexpr (!kNf4Codes<FMT>) {
@@ -1117,8 +1128,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       pr1 = *reinterpret_cast<const float2*>(s1.p + b);
     }
   };
+  // OCT (plain NF4, the wave's steps a whole number of eights): each lane
+  // loads 8 consecutive absmax of each row (32 B) per eight K steps: lane
+  // half hh blocks 2 ks + 8 hh .. +7, so the lane pair covers the trip's 16
+  // blocks.  Per-step absmax loads would touch each row's absmax line once
+  // per two steps, and at long K loops the L2 evicts the line in between
+  // (the counter runs showed each absmax byte fetched 4-7 times); here a
+  // line is touched once per 8 steps.  At trip step j < 4 one
+  // v_permlane32_swap per row of values j of the pair's chunk gives every
+  // lane its block of step j and, in the swap's second result, of step
+  // j + 4.
+  float4 q0a = {}, q0b = {}, q1a = {}, q1b = {};
+  auto fetch_oct = [&](int ks) {
+    if constexpr (AB == 8) {
+      const int b = ks < ks1 ? 2 * ks + 8 * hh : 0;
+      q0a = *reinterpret_cast<const float4*>(s0.p + b);
+      q0b = *reinterpret_cast<const float4*>(s0.p + b + 4);
+      q1a = *reinterpret_cast<const float4*>(s1.p + b);
+      q1b = *reinterpret_cast<const float4*>(s1.p + b + 4);
+    }
+  };
   auto fetch_step = [&](StreamCodes<FMT>& c0, StreamCodes<FMT>& c1, int ks) {
-    if constexpr (PAIR) {
+    if constexpr (AB != 0) {
       c0.fetch_codes(q0, ks * kStep, hh, K, ks < ks1);
       c1.fetch_codes(q1, ks * kStep, hh, K, ks < ks1);
     } else {
@@ -1128,6 +1159,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   };
   fetch_step(ca0, ca1, ks0);
   fetch_pair(ks0);
+  fetch_oct(ks0);
 
   // 4. the expert's assignments in ascending order: chunk c = a / 64 is
   //    wave c % NW's j = c / NW values
@@ -1156,6 +1188,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     if (g > 0) {
       fetch_step(ca0, ca1, ks0);
       fetch_pair(ks0);
+      fetch_oct(ks0);
     }
 
     f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
@@ -1175,8 +1208,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     // load in-range addresses and are zeroed through their scale.
     bf16x8 xa[kS];
     float nx0 = 0.0f, nx1 = 0.0f;  // PAIR: the second step's absmax, after the swap
-    // second: the step is the second of its trip (ks - ks0 odd)
-    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, bool second) {
+    float o0[4] = {}, o1[4] = {};  // OCT: the absmax of trip steps 4 .. 7, from the swaps of steps 0 .. 3
+    auto oct_at = [](const float4& a, const float4& b, int i) {
+      return i < 4 ? (i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w)
+                   : (i == 4 ? b.x : i == 5 ? b.y : i == 6 ? b.z : b.w);
+    };
+    // j: the step's place in its trip (ks - ks0 = j mod kTrip)
+    auto kstep = [&](int ks, StreamCodes<FMT>& sc0, StreamCodes<FMT>& sc1, int j) {
+      const bool second = (j & 1) != 0;
       // keep each step's arithmetic after the previous step's (hoisting it
       // would wait for codes that are still loading)
       __builtin_amdgcn_sched_barrier(0);
@@ -1194,6 +1233,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
           sc1.raw.scale = {nx1};
         }
       }
+      if constexpr (AB == 8) {
+        if (j < 4) {
+          const auto sw0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(oct_at(q0a, q0b, 2 * j)),
+                                                            __float_as_uint(oct_at(q0a, q0b, 2 * j + 1)), false, false);
+          const auto sw1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(oct_at(q1a, q1b, 2 * j)),
+                                                            __float_as_uint(oct_at(q1a, q1b, 2 * j + 1)), false, false);
+          sc0.raw.scale = {__uint_as_float(sw0[0])};
+          sc1.raw.scale = {__uint_as_float(sw1[0])};
+          o0[j] = __uint_as_float(sw0[1]);
+          o1[j] = __uint_as_float(sw1[1]);
+        } else {
+          sc0.raw.scale = {o0[j - 4]};
+          sc1.raw.scale = {o1[j - 4]};
+        }
+      }
       const RowCodes<FMT> c0 = sc0.use(), c1 = sc1.use();
       Dequant<FMT> d0, d1;
       d0.prepare(c0);
@@ -1206,6 +1260,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       }
       fetch_step(sc0, sc1, ks + 2);
       if (!second) fetch_pair(ks + 2);
+      // the chunk registers are free after the swap of trip step 3: the next
+      // trip's chunk loads from step 4 on
+      if (j == 4) fetch_oct(ks - 4 + kTrip);
     };
     {
       const bf16x8* p0 = bptr(ks0);
@@ -1213,15 +1270,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       for (int s_ = 0; s_ < kS; ++s_) xa[s_] = p0[s_];
     }
     fetch_step(cb0, cb1, ks0 + 1);
-    // Two steps per trip, register sets alternating, with no branch between
-    // them (a branch there would make the compiler copy or re-load register
-    // sets that are still loading, forcing full waits).  Parts are whole
-    // pairs of steps, so only the last part of an odd step count runs a
-    // trailing step past the range: its scale is zero, its A operand exactly
-    // zero, and it adds nothing.
-    for (int ks = ks0; ks < ks1; ks += 2) {
-      kstep(ks, ca0, ca1, false);
-      kstep(ks + 1, cb0, cb1, true);
+    // Two steps per trip (eight with OCT absmax), register sets alternating,
+    // with no branch between them (a branch there would make the compiler
+    // copy or re-load register sets that are still loading, forcing full
+    // waits).  Parts are whole pairs (eights) of steps, so only the last part
+    // of an odd step count runs a trailing step past the range: its scale is
+    // zero, its A operand exactly zero, and it adds nothing.
+    if constexpr (AB == 8) {
+      for (int ks = ks0; ks < ks1; ks += 8) {
+        kstep(ks, ca0, ca1, 0);
+        kstep(ks + 1, cb0, cb1, 1);
+        kstep(ks + 2, ca0, ca1, 2);
+        kstep(ks + 3, cb0, cb1, 3);
+        kstep(ks + 4, ca0, ca1, 4);
+        kstep(ks + 5, cb0, cb1, 5);
+        kstep(ks + 6, ca0, ca1, 6);
+        kstep(ks + 7, cb0, cb1, 7);
+      }
+    } else {
+      for (int ks = ks0; ks < ks1; ks += 2) {
+        kstep(ks, ca0, ca1, 0);
+        kstep(ks + 1, cb0, cb1, 1);
+      }
     }
 
     // the P partial sums of each row block, added in part order
@@ -1722,13 +1792,22 @@ void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const
                         const uint8_t* scc, hipStream_t s) {
   const int32_t n = a.T * a.K;
   const DecodeShape d = decode_shape(ux, G1 ? a.I / 32 : a.H / 64);
-  bool pair = false;
-  if constexpr (FMT == MOEQ_FMT_NF4) pair = ((G1 ? a.H : a.I) / kNf4Block) % 2 == 0;
-  if (pair)
-    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+  // plain NF4 absmax: in eights when the parts are equal whole eights of K
+  // steps (K a multiple of 1024, so the 16-byte chunk loads are aligned and
+  // in the row; the kernel splits K the same way), else in pairs when the
+  // row holds an even number of blocks
+  const int Kr = G1 ? a.H : a.I;
+  int ab = 0;
+  if constexpr (FMT == MOEQ_FMT_NF4)
+    ab = (Kr % 1024 == 0 && (Kr / 128) % (8 * d.p) == 0) ? 8 : ((Kr / kNf4Block) % 2 == 0 ? 2 : 0);
+  if (ab == 8)
+    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 8 : 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
+  else if (ab == 2)
+    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 2 : 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
         act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
   else
-    decode_kernel<FMT, G1, kWaves, false><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+    decode_kernel<FMT, G1, kWaves, 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
         act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
 }
 

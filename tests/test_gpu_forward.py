@@ -181,12 +181,19 @@ def test_forward_is_bit_identical_run_to_run():
     assert torch.equal(d1, d2)
     assert torch.equal(d3, d1[:32])
     # The two paths add the K products in different orders, and the tiled
-    # path rounds each weighted product to bf16 before the sum; each is within
-    # TOL of the oracle (tested above), so they agree within TOL.
+    # path rounds each weighted product to bf16 before the sum.  Each is
+    # within TOL of the oracle (tested above), which by the triangle
+    # inequality only bounds their gap by 2 TOL.  The gap itself is that
+    # rounding: independent errors of at most 2^-8 of each weighted row
+    # (bf16 round to nearest), about 2^-8 / sqrt(3) = 2.3e-3 of the rows in
+    # root mean square, and the K rows of a token add with little
+    # cancellation here (positive softmax weights over independent
+    # experts), so the gap is expected near 2.3e-3 (measured 2.7e-3).  The
+    # assertion allows twice that expectation (4.5e-3, inside TOL).
     err = rel_frobenius(bf16_to_f32(host_bits(d1)).astype(np.float64),
                         bf16_to_f32(host_bits(a[100:164])).astype(np.float64))
     print(f"few-assignment vs tiled path: rel Frobenius {err:.3e}")
-    assert err <= TOL
+    assert err <= 2 * 2.0 ** -8 / np.sqrt(3.0)
 
 
 def test_forward_rejects_mixed_formats():
