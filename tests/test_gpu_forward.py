@@ -100,6 +100,35 @@ def test_forward_nf4_block_counts(H, I, T):
     _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"nf4 H={H} I={I} T={T}")
 
 
+# The path boundary: T*K = 512 is the last few-assignment batch, 514 the
+# first tiled one; every output element of both is checked.
+@pytest.mark.parametrize("T", [256, 257])
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+def test_forward_path_boundary_full(fmt, T):
+    s = syn.SHAPES["tiny"]
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    say(f"forward path boundary fmt={fmt} T={T} (T*K={T * s.K})")
+    qg, qd = _quantize(gu, fmt), _quantize(dn, fmt)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    torch.cuda.synchronize()
+    _compare(x, idx, wts, gu, dn, fmt, out, np.arange(T), label=f"boundary {fmt} T={T}")
+
+
+# The largest expert count: 1024 experts (32 bitmap words in the
+# few-assignment path, 1024 per-expert tile counts in the routing), on both
+# paths, every output element.
+@pytest.mark.parametrize("T", [100, 600])
+def test_forward_max_experts_full(T):
+    s = syn.MoEShape("wide", E=1024, H=128, I=64, K=2, fmt="nf4")
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    assert int(idx.max()) >= 900  # the high experts are used
+    say(f"forward E={s.E} T={T}")
+    qg, qd = moeq.moeq_quantize_nf4(gu), moeq.moeq_quantize_nf4(dn)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    torch.cuda.synchronize()
+    _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"E={s.E} T={T}")
+
+
 # T*K = 387 takes the few-assignment path, 900 the tiled one
 @pytest.mark.parametrize("T", [129, 300])
 @pytest.mark.parametrize("fmt", ["nf4", "int8"])
