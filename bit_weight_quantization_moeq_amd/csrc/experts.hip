@@ -1705,41 +1705,54 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
                                                       C);
     return;
   }
+  if constexpr (MODE == 1) {
+    // dh = w * acc through LDS, then the SwiGLU backward row by row: a
+    // thread takes 4 consecutive columns of a row, so the loads of the saved
+    // fp32 g and u and the stores of bf16 dg and du cover whole rows (from
+    // the accumulator layout each such load touched 32 rows).  The same
+    // fp32 operations in the same order as element by element.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int r = tw + 32 * b + l32;
-    if (r >= nrows) continue;
-    const int64_t p = row0 + r;
+    for (int b = 0; b < 4; ++b) {
+      const float w = sw[tw + 32 * b + l32];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = c0 + cw + 32 * m + 8 * q + 4 * hh;
-        if (c >= C) continue;
-        const f32x16& a = acc[m][b];
-        if constexpr (MODE == 1) {
-          const float w = sw[r];
-          const float4 g4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + c);
-          const float4 u4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + C + c);
-          const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-          float dg[4], du[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dh = w * a[4 * q + i];
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
-            du[i] = dh * gv[i] * sg;
-            dg[i] = dh * uv[i] * sg * (1.0f + gv[i] * (1.0f - sg));
-          }
-          uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
-          *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(out) + p * C + c) =
-              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[m][b];
+          *reinterpret_cast<float4*>(smem + (tw + 32 * b + l32) * kOutPitch + 4 * (cw + 32 * m + 8 * q + 4 * hh)) =
+              make_float4(w * a[4 * q], w * a[4 * q + 1], w * a[4 * q + 2], w * a[4 * q + 3]);
         }
+    }
+    __syncthreads();
+    constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row
+#pragma unroll 4
+    for (int u = 0; u < kBM * kChunks / kThreads; ++u) {
+      const int i = threadIdx.x + u * kThreads, r = i / kChunks, k4 = i - r * kChunks;
+      const int c = c0 + 4 * k4;
+      if (r < nrows && c < C) {
+        const int64_t p = row0 + r;
+        const float4 d4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
+        const float4 g4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + c);
+        const float4 u4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + C + c);
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w},
+                    uv[4] = {u4.x, u4.y, u4.z, u4.w};
+        float dg[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
+          du[e] = dv[e] * gv[e] * sg;
+          dg[e] = dv[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+        }
+        uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+        *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
       }
     }
+    return;
   }
+  static_assert(MODE == 1 || MODE == 2, "T1 or T2");
 }
 
 // grad_w[a] = dout[a / K] . z[slot[a]] (0 for an unrouted assignment), one
