@@ -116,6 +116,9 @@ struct ForwardArgs {
 };
 // events: NULL or 5 events recorded at the stage boundaries.
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
+// The few-assignment (decode) forward, n = T*K <= 512 (decode.hip); called by
+// launch_experts_forward.
+hipError_t launch_experts_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
 
 struct BackwardArgs {
   const uint16_t* x;        // [T][H]

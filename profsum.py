@@ -46,7 +46,8 @@ import sys
 
 PKG = "bit_weight_quantization_moeq_amd"
 SOURCES = tuple(f"{PKG}/csrc/{n}" for n in (
-    "experts.hip", "quant.hip", "route.hip", "api.hip", "router.hip", "moeq_internal.h"))
+    "experts.hip", "decode.hip", "quant.hip", "route.hip", "api.hip", "router.hip", "experts_core.h",
+    "moeq_internal.h"))
 
 
 def _code_only(text):
@@ -63,20 +64,32 @@ def _kernel_file(kernel):
     here = os.path.dirname(os.path.abspath(__file__))
     base = kernel.split("@", 1)[0].split("<", 1)[0].strip()
     for rel in SOURCES:
-        if rel.endswith(".hip"):
-            with open(os.path.join(here, rel)) as f:
-                if re.search(r"__global__[^;{]*\b" + re.escape(base) + r"\s*\(", f.read()):
-                    return rel
+        with open(os.path.join(here, rel)) as f:
+            if re.search(r"__global__[^;{]*\b" + re.escape(base) + r"\s*\(", f.read()):
+                return rel
     return None
+
+
+def _with_includes(rel):
+    """`rel` and the csrc headers it includes, transitively, in first-seen order."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = [rel]
+    for cur in out:
+        with open(os.path.join(here, cur)) as f:
+            for name in re.findall(r'#include "([^"]+)"', f.read()):
+                inc = f"{PKG}/csrc/{name}"
+                if inc not in out and os.path.exists(os.path.join(here, inc)):
+                    out.append(inc)
+    return out
 
 
 def source_hash(kernel=None):
     """SHA-256 of the kernel sources' code (comments and layout ignored): of
-    the file that defines `kernel` plus the shared internal header, or of
+    the file that defines `kernel` plus the csrc headers it includes, or of
     every source when no kernel is named (or its file is not found)."""
     here = os.path.dirname(os.path.abspath(__file__))
     f = _kernel_file(kernel) if kernel else None
-    files = (f, f"{PKG}/csrc/moeq_internal.h") if f else SOURCES
+    files = _with_includes(f) if f else SOURCES
     h = hashlib.sha256()
     for rel in files:
         with open(os.path.join(here, rel)) as fh:
