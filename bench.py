@@ -486,9 +486,17 @@ def router_record(torch, moeq, syn, s, x, dev, copy_GBps, reps=20):
     w = torch.empty((T, s.K), dtype=torch.float32, device=dev)
     ms = timed(torch, lambda: moeq.moeq_router_topk(x, gate, s.K, top_k_index=idx, top_k_weights=w), reps)
     nbytes = 2.0 * T * s.H + 2.0 * s.E * s.H + 8.0 * T * s.K
+    # the router fused with the routing stage, against the router followed by
+    # the routing stage on its output (the same counts, offsets, perm, slot)
+    ws = torch.empty(moeq.moeq_router_route_workspace_bytes(T, s.H, s.E, s.K), dtype=torch.uint8, device=dev)
+    fused_ms = timed(torch, lambda: moeq.moeq_router_route(x, gate, s.K, workspace=ws), reps)
+    rws = torch.empty(moeq.moeq_route_workspace_bytes(T, s.K, s.E), dtype=torch.uint8, device=dev)
+    split_ms = timed(torch, lambda: moeq.moeq_route_buckets(
+        moeq.moeq_router_topk(x, gate, s.K, top_k_index=idx, top_k_weights=w)[0], s.E, workspace=rws), reps)
     return {"workload": f"T={T}, gate [{s.E}, {s.H}] bf16, top-{s.K}", "ms": ms,
             "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "TFLOPs": 2.0 * T * s.E * s.H / (ms * 1e-3) / 1e12}
+            "TFLOPs": 2.0 * T * s.E * s.H / (ms * 1e-3) / 1e12,
+            "fused_with_routing_ms": fused_ms, "router_then_routing_ms": split_ms}
 
 
 def offload_record(torch, moeq, s, qg, qd, x, idx, wts, dev, fwd_ms, layers=4, passes=2):

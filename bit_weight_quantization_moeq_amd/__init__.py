@@ -21,6 +21,7 @@ __all__ = [
     "moeq_experts_forward_workspace_bytes", "moeq_experts_forward",
     "moeq_route_workspace_bytes", "moeq_route_buckets", "library_path",
     "moeq_experts_backward_workspace_bytes", "moeq_experts_backward", "moeq_router_topk",
+    "moeq_router_route_workspace_bytes",
     "moeq_qweight_copy_async", "FMT_NF4_DQ", "DQ_GROUP", "moeq_compress_absmax",
     "moeq_stream_reference", "moeq_router_route", "moeq_experts_forward_routed", "Routing",
     "moeq_experts_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -529,6 +530,12 @@ class Routing:
 
     def __iter__(self):
         return iter((self.counts, self.offsets, self.perm, self.slot))
+
+
+def moeq_router_route_workspace_bytes(T, H, E, K):
+    """Workspace bytes :func:`moeq_router_route` needs for T tokens, hidden
+    size H, E experts and top-K."""
+    return int(_load().moeq_router_route_workspace_bytes(int(T), int(H), int(E), int(K)))
 
 
 def moeq_router_route(hidden, gate, K, renormalize=False, workspace=None, stream=None):
