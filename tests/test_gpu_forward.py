@@ -114,19 +114,22 @@ def test_forward_path_boundary_full(fmt, T):
     _compare(x, idx, wts, gu, dn, fmt, out, np.arange(T), label=f"boundary {fmt} T={T}")
 
 
-# The largest expert count: 1024 experts (32 bitmap words in the
-# few-assignment path, 1024 per-expert tile counts in the routing), on both
-# paths, every output element.
+# The expert-count extremes on both paths, every output element: 1024
+# experts (32 bitmap words in the few-assignment path, 1024 per-expert tile
+# counts in the routing) and a single expert with top-1 (every assignment in
+# one expert: one workgroup's list holds them all, the tiles cover them all).
 @pytest.mark.parametrize("T", [100, 600])
-def test_forward_max_experts_full(T):
-    s = syn.MoEShape("wide", E=1024, H=128, I=64, K=2, fmt="nf4")
+@pytest.mark.parametrize("E,K", [(1024, 2), (1, 1)])
+def test_forward_expert_count_extremes_full(E, K, T):
+    s = syn.MoEShape("wide", E=E, H=128, I=64, K=K, fmt="nf4")
     gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
-    assert int(idx.max()) >= 900  # the high experts are used
-    say(f"forward E={s.E} T={T}")
+    if E > 1:
+        assert int(idx.max()) >= 900  # the high experts are used
+    say(f"forward E={s.E} K={K} T={T}")
     qg, qd = moeq.moeq_quantize_nf4(gu), moeq.moeq_quantize_nf4(dn)
     out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
     torch.cuda.synchronize()
-    _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"E={s.E} T={T}")
+    _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"E={s.E} K={K} T={T}")
 
 
 # T*K = 387 takes the few-assignment path, 900 the tiled one
