@@ -104,13 +104,24 @@ def _check(status, where):
         raise MoeqError(status, where)
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+# The current stream's raw handle without building a Stream object (the
+# public current_stream() costs a few microseconds of host time per call).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device=None):
+    """Raw hipStream_t: ``stream``'s, else the current stream of ``device``
+    (a CUDA device of the call's tensors), else of the current device."""
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is not None and device is not None and device.index is not None:
+        return ctypes.c_void_p(_raw_stream(device.index))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """A tensor's device address for a c_void_p argument (None: NULL)."""
+    return t.data_ptr() if t is not None else None
 
 
 def _dev(t, dtype, name, shape=None):
@@ -122,8 +133,10 @@ def _dev(t, dtype, name, shape=None):
     structural check (:func:`_on_device`)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if shape is not None and tuple(t.shape) != tuple(int(d) for d in shape):
-        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
+    if shape is not None and t.shape != shape:
+        want = tuple(int(d) for d in shape)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -133,12 +146,19 @@ def _dev(t, dtype, name, shape=None):
 
 def _on_device(where, *tensors):
     """Every tensor is a CUDA (HIP) tensor, all on one device."""
-    ts = [t for t in tensors if t is not None]
-    for t in ts:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
         if not t.is_cuda:
             raise TypeError(f"{where}: every tensor must be a CUDA (HIP) tensor")
-    if len({t.device for t in ts}) > 1:
-        raise ValueError(f"{where}: tensors on different devices {sorted({str(t.device) for t in ts})}")
+        d = t.device
+        if dev is None:
+            dev = d
+        elif d != dev:
+            ds = sorted({str(u.device) for u in tensors if u is not None})
+            raise ValueError(f"{where}: tensors on different devices {ds}")
+    return dev
 
 
 def _match_qweight(q, shape, formats, name):
@@ -275,9 +295,9 @@ class QWeight:
             t = getattr(self, name)
             if not isinstance(t, torch.Tensor):
                 raise TypeError(f"QWeight.{name} must be a torch tensor")
-            if t.numel() != int(torch.Size(shape).numel()):
-                raise ValueError(f"QWeight.{name} must hold {shape} ({torch.Size(shape).numel()} elements), "
-                                 f"got {tuple(t.shape)}")
+            n = shape[0] * shape[1] * (shape[2] if len(shape) == 3 else 1)
+            if t.numel() != n:
+                raise ValueError(f"QWeight.{name} must hold {shape} ({n} elements), got {tuple(t.shape)}")
             if t.dtype != dtype:
                 raise TypeError(f"QWeight.{name} must be {dtype}, got {t.dtype}")
             if not t.is_contiguous():
@@ -299,6 +319,10 @@ class QWeight:
 
     def _c(self, allow_host=False):
         self.validate(allow_host)
+        return self._desc()
+
+    def _desc(self):
+        """The C descriptor, for a caller that has validated this QWeight."""
         codes = self.scale_codes.data_ptr() if self.scale_codes is not None else None
         return _QW(self.format, self.num_experts, self.rows, self.cols, self.blocksize,
                    self.qdata.data_ptr(), self.scales.data_ptr(), codes)
@@ -419,15 +443,15 @@ def moeq_experts_forward(hidden, top_k_index, top_k_weights, gate_up, down, out=
     if out is not None:
         _dev(out, torch.bfloat16, "out", (T, H))
     wt = _forward_weights(gate_up, down, H)
-    _on_device("moeq_experts_forward", hidden, top_k_index, top_k_weights, out, *wt)
+    dev = _on_device("moeq_experts_forward", hidden, top_k_index, top_k_weights, out, *wt)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
-    gu, dn = gate_up._c(), down._c()
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
     lib = _load()
-    need = int(lib.moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
-    workspace = _workspace(workspace, need, hidden.device)
-    args = (_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K), ctypes.byref(gu),
-            ctypes.byref(dn), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    need = int(lib.moeq_experts_forward_workspace_bytes(T, K, ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, dev)
+    args = (_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), T, K, ctypes.byref(gu),
+            ctypes.byref(dn), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream, dev))
     if stage_events is None:
         _check(lib.moeq_experts_forward(*args), "moeq_experts_forward")
     else:
@@ -448,11 +472,11 @@ def moeq_experts_forward_noalloc(hidden, top_k_index, top_k_weights, gate_up, do
     T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
     _dev(out, torch.bfloat16, "out", (T, H))
     wt = _forward_weights(gate_up, down, H)
-    _on_device("moeq_experts_forward_noalloc", hidden, top_k_index, top_k_weights, out, *wt)
-    gu, dn = gate_up._c(), down._c()
-    _check(_load().moeq_experts_forward_noalloc(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T),
-                                                int(K), ctypes.byref(gu), ctypes.byref(dn), _ptr(out),
-                                                _stream(stream)), "moeq_experts_forward_noalloc")
+    dev = _on_device("moeq_experts_forward_noalloc", hidden, top_k_index, top_k_weights, out, *wt)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
+    _check(_load().moeq_experts_forward_noalloc(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), T,
+                                                K, ctypes.byref(gu), ctypes.byref(dn), _ptr(out),
+                                                _stream(stream, dev)), "moeq_experts_forward_noalloc")
     return out
 
 
@@ -474,19 +498,19 @@ def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, gra
     if grad_weights is not None:
         _dev(grad_weights, torch.float32, "grad_weights", (T, K))
     wt = _forward_weights(gate_up, down, H)
-    _on_device("moeq_experts_backward", hidden, top_k_index, top_k_weights, grad_out, grad_hidden,
-               grad_weights, *wt)
+    dev = _on_device("moeq_experts_backward", hidden, top_k_index, top_k_weights, grad_out, grad_hidden,
+                     grad_weights, *wt)
     if grad_hidden is None:
-        grad_hidden = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+        grad_hidden = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     if grad_weights is None:
-        grad_weights = torch.empty((T, K), dtype=torch.float32, device=hidden.device)
-    gu, dn = gate_up._c(), down._c()
+        grad_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
     lib = _load()
-    need = int(lib.moeq_experts_backward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
-    workspace = _workspace(workspace, need, hidden.device)
-    _check(lib.moeq_experts_backward(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
+    need = int(lib.moeq_experts_backward_workspace_bytes(T, K, ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, dev)
+    _check(lib.moeq_experts_backward(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), T, K,
                                      ctypes.byref(gu), ctypes.byref(dn), _ptr(grad_out), _ptr(grad_hidden),
-                                     _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream)),
+                                     _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
            "moeq_experts_backward")
     return grad_hidden, grad_weights
 
@@ -583,18 +607,18 @@ def moeq_experts_forward_routed(hidden, top_k_index, top_k_weights, gate_up, dow
     if out is not None:
         _dev(out, torch.bfloat16, "out", (T, H))
     wt = _forward_weights(gate_up, down, H)
-    _on_device("moeq_experts_forward_routed", hidden, top_k_index, top_k_weights, out, routing.offsets,
-               routing.perm, routing.slot, *wt)
+    dev = _on_device("moeq_experts_forward_routed", hidden, top_k_index, top_k_weights, out, routing.offsets,
+                     routing.perm, routing.slot, *wt)
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
-    gu, dn = gate_up._c(), down._c()
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
     lib = _load()
-    need = int(lib.moeq_experts_forward_workspace_bytes(int(T), int(K), ctypes.byref(gu), ctypes.byref(dn)))
-    workspace = _workspace(workspace, need, hidden.device)
-    _check(lib.moeq_experts_forward_routed(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), int(T), int(K),
+    need = int(lib.moeq_experts_forward_workspace_bytes(T, K, ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, dev)
+    _check(lib.moeq_experts_forward_routed(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), T, K,
                                            ctypes.byref(gu), ctypes.byref(dn), _ptr(routing.offsets),
                                            _ptr(routing.perm), _ptr(routing.slot), _ptr(out), _ptr(workspace),
-                                           workspace.numel(), _stream(stream)), "moeq_experts_forward_routed")
+                                           workspace.numel(), _stream(stream, dev)), "moeq_experts_forward_routed")
     return out
 
 
