@@ -81,7 +81,7 @@ Layout layout(int64_t n, int32_t E, int64_t I, int64_t H) {
   L.perm = o;         o += up(sizeof(int32_t) * (size_t)n);
   L.slot = o;         o += up(sizeof(int32_t) * (size_t)n);
   L.h = o;            o += up(sizeof(uint16_t) * (size_t)(n * I));
-  L.y = o;            o += up(sizeof(float) * (size_t)(n * H));
+  L.y = o;            o += up(sizeof(float) * (size_t)(n * H) * (size_t)decode_down_splits(n, E, H, I));
   L.total = o;
   return L;
 }

@@ -99,6 +99,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   const int nrb = G1 ? I / 32 : H / 64;  // row blocks of the expert
   const int RB = NW / P;
   const int rbi = blockIdx.y * RB + wave / P, part = wave % P;
+  // K is split into PZ = P * gridDim.z parts: P within the workgroup (their
+  // sums added in LDS below) times gridDim.z across workgroups (each writing
+  // its own slice of y, added by the combine)
+  const int PZ = P * (int)gridDim.z, zpart = (int)blockIdx.z * P + part;
   const bool on = rbi < nrb;  // a wave past the last row block streams block 0 and stores nothing
   const int col0 = (on ? rbi : 0) * (G1 ? 32 : 64);
   const int R = G1 ? 2 * I : H;  // rows per expert
@@ -109,15 +113,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, R, r0, K, 0);
   const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, R, r1, K, 0);
   // Parts are whole groups of gran K steps: eights when K is a multiple of
-  // 1024 and the P parts split the steps into equal eights (the condition
+  // 1024 and the PZ parts split the steps into equal eights (the condition
   // under which the host picks AB = 8), else pairs.  The split depends on
   // the shape only, not on AB, so every format sums the same parts.
   constexpr int kTrip = AB == 8 ? 8 : 2;  // steps per loop trip
   constexpr bool PAIR = AB == 2;
   const int nks = (K + kStep - 1) / kStep;
-  const int gran = (K % 1024 == 0 && nks % (8 * P) == 0) ? 8 : 2;
+  const int gran = (K % 1024 == 0 && nks % (8 * PZ) == 0) ? 8 : 2;
   const int nkp = (nks + gran - 1) / gran;  // groups of steps
-  const int ks0 = gran * (part * nkp / P), ks1 = min(gran * ((part + 1) * nkp / P), nks);
+  const int ks0 = gran * (zpart * nkp / PZ), ks1 = min(gran * ((zpart + 1) * nkp / PZ), nks);
   // int8: the row scales, first of this wave's loads
   float rs0 = 0.0f, rs1 = 0.0f;
   if constexpr (!kNf4Codes<FMT>) {
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
         }
       } else {
         const float wr = wts[a];
-        float* yp = yout + (int64_t)a * H + col0 + 4 * hh;
+        float* yp = yout + ((int64_t)blockIdx.z * n + a) * H + col0 + 4 * hh;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           *reinterpret_cast<float4*>(yp + 8 * q) =
@@ -362,12 +366,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
 }
 
 // Decode combine: out[t] = bf16(sum over k in order of y[t*K + k]), skipping
-// unrouted assignments.  One workgroup per token: the routing entries are
-// read once into LDS, then each thread keeps the y loads of up to 8
-// assignments in flight at once.
+// unrouted assignments, where y[a] is the sum over z in order of the Z slices
+// y_z[a] (the down launch's parts of K across workgroups; Z = 1, 2 or 4).
+// One workgroup per token: the routing entries are read once into LDS, then
+// each thread keeps 8 y loads (8 / Z assignments) in flight at once.
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* __restrict__ y,
                                                                  const int32_t* __restrict__ idx, int32_t K,
-                                                                 int32_t E, int32_t H, uint16_t* __restrict__ out) {
+                                                                 int32_t E, int32_t H, int32_t zlog,
+                                                                 int64_t zstride, uint16_t* __restrict__ out) {
   __shared__ uint8_t routed[kDecodeMax];
   const int64_t tok = blockIdx.x;
   for (int k = threadIdx.x; k < K; k += kThreads) {
@@ -375,21 +381,30 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* _
     routed[k] = e >= 0 && e < E;
   }
   __syncthreads();
+  const int Z = 1 << zlog, kc = 8 >> zlog;
   for (int n4 = threadIdx.x; n4 < H / 4; n4 += kThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = 0; k0 < K; k0 += 8) {
+    for (int k0 = 0; k0 < K; k0 += kc) {
       bool use[8];
       float4 v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        use[j] = k0 + j < K && routed[k0 + j];
-        v[j] = use[j] ? *reinterpret_cast<const float4*>(y + (tok * K + k0 + j) * H + 4 * n4)
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + (u >> zlog), z = u & (Z - 1);
+        use[u] = (u >> zlog) < kc && k < K && routed[k];
+        v[u] = use[u] ? *reinterpret_cast<const float4*>(y + z * zstride + (tok * K + k) * H + 4 * n4)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      float4 sk = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (use[j]) {
-          acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
+      for (int u = 0; u < 8; ++u) {
+        const int z = u & (Z - 1);
+        if (z == 0) {
+          sk = v[u];
+        } else {
+          sk.x += v[u].x; sk.y += v[u].y; sk.z += v[u].z; sk.w += v[u].w;
+        }
+        if (z == Z - 1 && use[u]) {
+          acc.x += sk.x; acc.y += sk.y; acc.z += sk.z; acc.w += sk.w;
         }
       }
     }
@@ -413,11 +428,25 @@ DecodeShape decode_shape(int ux, int nrb) {
   return {p, rb, (nrb + rb - 1) / rb};
 }
 
+// Parts of K across workgroups (grid z) for the down launch: when even P = 4
+// leaves the chip short of waves (few touched experts, e.g. one token of a
+// top-2 layer), K is split further, 2 or 4 ways, while every part keeps at
+// least a pair of K steps (counted in 128-wide steps for every format, so
+// that the workspace size depends on the shape alone).
+int decode_z(int ux, int nrb, int p, int64_t I) {
+  const int nkp = (int)((I / 128 + 1) / 2);
+  int z = 1;
+  while (p == kWaves && z < 4 && (long)ux * nrb * p * z < 1536 && p * z * 2 <= nkp) z *= 2;
+  return z;
+}
+
 template <int FMT, bool G1>
 void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const uint8_t* q, const float* sc,
                         const uint8_t* scc, hipStream_t s) {
   const int32_t n = a.T * a.K;
   const DecodeShape d = decode_shape(ux, G1 ? a.I / 32 : a.H / 64);
+  const int z = G1 ? 1 : decode_z(ux, a.H / 64, d.p, a.I);
+  const int pz = d.p * z;
   // plain NF4 absmax: in eights when the parts are equal whole eights of K
   // steps (K a multiple of 1024, so the 16-byte chunk loads are aligned and
   // in the row; the kernel splits K the same way), else in pairs when the
@@ -425,15 +454,16 @@ void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const
   const int Kr = G1 ? a.H : a.I;
   int ab = 0;
   if constexpr (FMT == MOEQ_FMT_NF4)
-    ab = (Kr % 1024 == 0 && (Kr / 128) % (8 * d.p) == 0) ? 8 : ((Kr / kNf4Block) % 2 == 0 ? 2 : 0);
+    ab = (Kr % 1024 == 0 && (Kr / 128) % (8 * pz) == 0) ? 8 : ((Kr / kNf4Block) % 2 == 0 ? 2 : 0);
+  const dim3 grid(ux, d.gy, z);
   if (ab == 8)
-    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 8 : 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 8 : 0><<<grid, kThreads, 0, s>>>(
         act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
   else if (ab == 2)
-    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 2 : 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+    decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 2 : 0><<<grid, kThreads, 0, s>>>(
         act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
   else
-    decode_kernel<FMT, G1, kWaves, 0><<<dim3(ux, d.gy), kThreads, 0, s>>>(
+    decode_kernel<FMT, G1, kWaves, 0><<<grid, kThreads, 0, s>>>(
         act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
 }
 
@@ -446,9 +476,17 @@ hipError_t launch_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* 
   if (ev) (void)hipEventRecord(ev[2], s);
   launch_decode_gemm<FMT, false>(a, ux, a.h, static_cast<const uint8_t*>(a.dn_q), a.dn_s, a.dn_c, s);
   if (ev) (void)hipEventRecord(ev[3], s);
-  decode_combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.idx, a.K, a.E, a.H, a.out);
+  const int z = decode_down_splits(n, a.E, a.H, a.I);
+  decode_combine_kernel<<<a.T, kThreads, 0, s>>>(a.y, a.idx, a.K, a.E, a.H, z == 4 ? 2 : (z == 2 ? 1 : 0),
+                                                 (int64_t)n * a.H, a.out);
   if (ev) (void)hipEventRecord(ev[4], s);
   return hipGetLastError();
+}
+
+int decode_down_splits(int64_t n, int32_t E, int64_t H, int64_t I) {
+  if (n > kDecodeMax || n < 1) return 1;
+  const int ux = E < n ? E : (int)n;
+  return decode_z(ux, (int)(H / 64), decode_shape(ux, (int)(H / 64)).p, I);
 }
 
 hipError_t launch_experts_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {

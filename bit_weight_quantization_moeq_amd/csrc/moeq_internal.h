@@ -119,6 +119,9 @@ hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_
 // The few-assignment (decode) forward, n = T*K <= 512 (decode.hip); called by
 // launch_experts_forward.
 hipError_t launch_experts_decode(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
+// Slices of y the few-assignment forward's down launch writes (1, 2 or 4: K
+// split across workgroups when few experts are touched); 1 off that path.
+int decode_down_splits(int64_t n, int32_t E, int64_t H, int64_t I);
 
 struct BackwardArgs {
   const uint16_t* x;        // [T][H]

@@ -110,6 +110,24 @@ def test_forward_double_quant(name, T, ns, nc):
     assert err <= TOL
 
 
+# Few touched experts and a long down K: the down launch splits K across
+# workgroups, the same way for both twins.
+def test_forward_double_quant_down_split():
+    s = syn.MoEShape("longk", E=2, H=256, I=4096, K=1, fmt="nf4")
+    T = 2
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    say("dq forward down split")
+    qg, qd = moeq.moeq_quantize_nf4(gu, double_quant=True), moeq.moeq_quantize_nf4(dn, double_quant=True)
+    out = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    twin = moeq.moeq_experts_forward(x, idx, wts, _decoded_nf4(qg), _decoded_nf4(qd))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), twin.view(torch.int16))
+    ref = experts_forward(host_bits(x), host(idx), host(wts), LazyDequant(gu, "nf4_dq"), LazyDequant(dn, "nf4_dq"))
+    err = rel_frobenius(bf16_to_f32(host_bits(out)).astype(np.float64), ref)
+    print(f"dq down split: rel Frobenius error {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("name,T,ns", [("tiny", 64, 64), ("olmoe", 1024, 2)])
 def test_backward_double_quant(name, T, ns):
     s, gu, dn, x, idx, wts = _layer(name, T)

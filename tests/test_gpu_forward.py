@@ -100,6 +100,20 @@ def test_forward_nf4_block_counts(H, I, T):
     _compare(x, idx, wts, gu, dn, "nf4", out, np.arange(T), label=f"nf4 H={H} I={I} T={T}")
 
 
+# Few touched experts and a long down K (E = 2, H = 256, I = 4096, top-1):
+# the down launch splits K across workgroups as well (4 ways here), each
+# writing its own slice of y for the combine to add; every output element.
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+@pytest.mark.parametrize("T", [1, 2])
+def test_forward_down_split_full(fmt, T):
+    s = syn.MoEShape("longk", E=2, H=256, I=4096, K=1, fmt=fmt)
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, T, device="cpu"))
+    say(f"forward down split fmt={fmt} T={T}")
+    out = moeq.moeq_experts_forward(x, idx, wts, _quantize(gu, fmt), _quantize(dn, fmt))
+    torch.cuda.synchronize()
+    _compare(x, idx, wts, gu, dn, fmt, out, np.arange(T), label=f"down split {fmt} T={T}")
+
+
 # The path boundary: T*K = 512 is the last few-assignment batch, 514 the
 # first tiled one; every output element of both is checked.
 @pytest.mark.parametrize("T", [256, 257])
