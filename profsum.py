@@ -230,7 +230,9 @@ def kernels(pmc_dir, command, prefix="moeq::"):
     ``counters``) and, from the SQ stall counters, the fractions of the
     waves' cycles spent waiting on a counter (SQ_WAIT_INST_ANY), waiting for
     anything (SQ_WAIT_ANY), issuing VALU (SQ_ACTIVE_INST_VALU, MFMA included)
-    and LDS (SQ_ACTIVE_INST_LDS) instructions."""
+    and LDS (SQ_ACTIVE_INST_LDS) instructions; with SQ_WAVES in the same run,
+    the instructions each wave issued (SQ_INSTS_VALU, MFMA included;
+    SQ_INSTS_VMEM_RD; SQ_INSTS_MFMA)."""
     agent = _gpu_agent(pmc_dir)
     simds = int(agent.get("Simd_Count", 0) or 0)
     nxcc = int(agent.get("Num_Xcc", 1) or 1)
@@ -246,8 +248,9 @@ def kernels(pmc_dir, command, prefix="moeq::"):
         for (_, name), c in acc.items():
             per.setdefault(short(name), []).append(c)
     print(f"command: `{command}`\n")
-    print("| kernel | dispatches | mean us | MFMA busy | clock GHz | wait on counter | wait any | VALU issue | LDS issue |")
-    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    print("| kernel | dispatches | mean us | MFMA busy | clock GHz | wait on counter | wait any | VALU issue | LDS issue "
+          "| VALU instr / wave | VMEM reads / wave | MFMA / wave |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
     rows = {}
     for k in sorted(per, key=lambda k: -sum(c["duration_ns"] for c in per[k])):
         cs = per[k]
@@ -261,9 +264,15 @@ def kernels(pmc_dir, command, prefix="moeq::"):
                            ("SQ_ACTIVE_INST_VALU", "valu"), ("SQ_ACTIVE_INST_LDS", "lds")):
                 if n in cs[0]:
                     row[key] = tot(n) / tot("SQ_WAVE_CYCLES")
+        if tot("SQ_WAVES") > 0:
+            for n, key in (("SQ_INSTS_VALU", "valu_per_wave"), ("SQ_INSTS_VMEM_RD", "vmem_rd_per_wave"),
+                           ("SQ_INSTS_MFMA", "mfma_per_wave")):
+                if n in cs[0]:
+                    row[key] = tot(n) / tot("SQ_WAVES")
         f = lambda key, fmt: (fmt.format(row[key]) if key in row else "")
         print(f"| {k} | {row['dispatches']} | {row['mean_us']:.1f} | {f('mfma_busy', '{:.1%}')} | {f('clock_GHz', '{:.2f}')} "
-              f"| {f('wait_counter', '{:.1%}')} | {f('wait_any', '{:.1%}')} | {f('valu', '{:.1%}')} | {f('lds', '{:.1%}')} |")
+              f"| {f('wait_counter', '{:.1%}')} | {f('wait_any', '{:.1%}')} | {f('valu', '{:.1%}')} | {f('lds', '{:.1%}')} "
+              f"| {f('valu_per_wave', '{:.0f}')} | {f('vmem_rd_per_wave', '{:.0f}')} | {f('mfma_per_wave', '{:.0f}')} |")
         rows[k] = row
     return rows
 

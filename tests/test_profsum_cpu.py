@@ -128,7 +128,10 @@ def test_kernels_table(tmp_path, capsys):
                               "SQ_WAVE_CYCLES": 200.0, "SQ_WAIT_INST_ANY": 50.0, "SQ_WAIT_ANY": 20.0,
                               "SQ_ACTIVE_INST_VALU": 100.0, "SQ_ACTIVE_INST_LDS": 10.0}),
                             (2, "void moeq::(anonymous namespace)::b_kernel<2>(int)", {"SQ_WAVE_CYCLES": 100.0,
-                                                                                    "SQ_WAIT_INST_ANY": 10.0}),
+                                                                                    "SQ_WAIT_INST_ANY": 10.0,
+                                                                                    "SQ_WAVES": 8.0,
+                                                                                    "SQ_INSTS_VALU": 400.0,
+                                                                                    "SQ_INSTS_VMEM_RD": 24.0}),
                             (3, "void at::native::fill(int)", {"SQ_WAVE_CYCLES": 5.0})):
         for n, v in ctr.items():
             rows.append({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": n, "Counter_Value": v,
@@ -142,4 +145,7 @@ def test_kernels_table(tmp_path, capsys):
     assert abs(a["mfma_busy"] - 0.25) < 1e-12 and abs(a["clock_GHz"] - 0.5) < 1e-12
     assert (a["wait_counter"], a["wait_any"], a["valu"], a["lds"]) == (0.25, 0.1, 0.5, 0.05)
     assert got["b_kernel<2>"]["wait_counter"] == 0.1 and "mfma_busy" not in got["b_kernel<2>"]
+    b = got["b_kernel<2>"]
+    assert (b["valu_per_wave"], b["vmem_rd_per_wave"]) == (50.0, 3.0) and "mfma_per_wave" not in b
+    assert "valu_per_wave" not in a  # no SQ_WAVES in its run
     assert a["mean_us"] == 2.0
