@@ -24,8 +24,11 @@ namespace {
 // dequantizes them in registers into the MFMA A operand and multiplies the
 // expert's token rows (at most 32 per pass, read from L2 as the B operand).
 // The P partial sums of a row block meet in LDS and are added in part order,
-// so the result does not depend on timing.  Rows of h and y are indexed by
-// assignment, so the combine needs no slot map.
+// so the result does not depend on timing.  When even P = 4 leaves the chip
+// short of waves, the down launch also splits K across workgroups (grid z,
+// Z = 2 or 4): each z slice writes its own copy of y, and the combine adds
+// the copies in z order.  Rows of h and y are indexed by assignment, so the
+// combine needs no slot map.
 //   G1 (gate_up): row block = gate rows jcol..+32 and up rows I+jcol..+32,
 //                 K = H, B rows x[a / K]; h[a][jcol..+32] = bf16(silu(g) * u).
 //   G2 (down):    row block = down rows ncol..+64, K = I, B rows h[a];
