@@ -250,7 +250,7 @@ def step_record(torch, np, moeq, syn, s, T, dev, steps, warmup, copy_GBps):
         "quantize_gate_up": ("hbm", n_gu * NF4_BYTES_PER_ELEM, "nf4_quantize_kernel"),
         "quantize_down": ("hbm", n_dn * NF4_BYTES_PER_ELEM, "nf4_quantize_kernel"),
         "g1_gate_up_swiglu": ("mfma", 4.0 * n_assign * s.H * s.I, "g1_kernel<1>"),
-        "g2_down": ("mfma", 2.0 * n_assign * s.H * s.I, "g2_kernel<1, unsigned short>"),
+        "g2_down": ("mfma", 2.0 * n_assign * s.H * s.I, "g2_kernel<1>"),
         "route": ("hbm", n_assign * 4 * 4.0, "route_rank_kernel"),
         "combine": ("hbm", n_assign * s.H * 2.0 + T * s.H * 2.0, "combine_kernel<unsigned short>"),
     }
@@ -461,7 +461,8 @@ def quantize_records(torch, np, moeq, syn, dev, copy_GBps, log, reps=5):
 def backward_record(torch, moeq, syn, s, qg, qd, x, idx, wts, dev, reps=10):
     """Gradients of the experts block (hidden states and routing weights, the
     packed weights frozen): the gate_up GEMM recomputed (4 T K H I flops), the
-    unweighted down GEMM (2), the down^T GEMM (2), the gate_up^T GEMM (4)."""
+    down^T GEMM (2), the gate_up^T GEMM (4); the routing-weight gradient comes
+    from the down^T product, with no down GEMM of its own."""
     T = x.shape[0]
     dout = syn.grad_output(T, s.H, device=dev)
     ws = torch.empty(moeq.moeq_experts_backward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
@@ -469,11 +470,11 @@ def backward_record(torch, moeq, syn, s, qg, qd, x, idx, wts, dev, reps=10):
     gw = torch.empty((T, s.K), dtype=torch.float32, device=dev)
     ms = timed(torch, lambda: moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout, grad_hidden=gx,
                                                          grad_weights=gw, workspace=ws), reps)
-    flops = 12.0 * T * s.K * s.H * s.I
+    flops = 10.0 * T * s.K * s.H * s.I
     return {"workload": f"{s.name}-shaped layer, T={T}, incoming gradient ~ N(0, 1) bf16",
             "ms": ms, "tokens_per_s": T / (ms * 1e-3), "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "flops": "12 T K H I (gate_up recompute 4, unweighted down 2, down^T 2, gate_up^T 4)"}
+            "flops": "10 T K H I (gate_up recompute 4, down^T 2, gate_up^T 4)"}
 
 
 def router_record(torch, moeq, syn, s, x, dev, copy_GBps, reps=20):

@@ -330,19 +330,20 @@ moeq_status moeq_experts_forward_routed(const uint16_t* x, const int32_t* idx, c
   return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream), nullptr));
 }
 
-// Backward workspace: the routing buffers, then h bf16 [n][I], g|u fp32
-// [n][2I], z / dx fp32 [n][H] and dg|du bf16 [n][2I], 256-B aligned.
+// Backward workspace: the routing buffers, then T1's grad_w shares fp32
+// [n][column tiles of I], g|u fp32 [n][2I], dx fp32 [n][H] and dg|du bf16
+// [n][2I], 256-B aligned.
 struct BwLayout {
   Layout route;
-  size_t h, gu, zdx, dgu, total;
+  size_t gwp, gu, dx, dgu, total;
 };
 BwLayout bw_layout(int64_t n, int32_t E, int64_t I, int64_t H) {
   BwLayout L;
   L.route = layout(n, E, 0, 0);
   size_t o = L.route.total;
-  L.h = o;   o += up(sizeof(uint16_t) * (size_t)(n * I));
+  L.gwp = o; o += up(sizeof(float) * (size_t)(n * backward_col_tiles((int32_t)I)));
   L.gu = o;  o += up(sizeof(float) * (size_t)(n * 2 * I));
-  L.zdx = o; o += up(sizeof(float) * (size_t)(n * H));
+  L.dx = o;  o += up(sizeof(float) * (size_t)(n * H));
   L.dgu = o; o += up(sizeof(uint16_t) * (size_t)(n * 2 * I));
   L.total = o;
   return L;
@@ -384,9 +385,9 @@ moeq_status moeq_experts_backward(const uint16_t* x, const int32_t* idx, const f
   a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
   a.grad_x = grad_x; a.grad_w = grad_w;
   a.rb = route_buffers(workspace, L.route);
-  a.h = reinterpret_cast<uint16_t*>(w + L.h);
+  a.gw_part = reinterpret_cast<float*>(w + L.gwp);
   a.gu_save = reinterpret_cast<float*>(w + L.gu);
-  a.zdx = reinterpret_cast<float*>(w + L.zdx);
+  a.dx = reinterpret_cast<float*>(w + L.dx);
   a.dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
   return device_status(launch_experts_backward(a, static_cast<hipStream_t>(stream)));
 }

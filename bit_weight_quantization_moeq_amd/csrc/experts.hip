@@ -91,8 +91,9 @@ __device__ __forceinline__ void g1_tile(char* sX, const uint16_t* x, const int32
   C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(x), roff, H, gq, gs, uq, us, wave_on, accG, accU);
   // lane holds, per token block b and register quad q, the four h columns
   // jcol + 8q + 4*hh + 0..3 of token row 32b + l32.
+  // (h == nullptr: the backward's recompute, which keeps g and u instead)
   const int l32 = lane & 31, hh = lane >> 5;
-  if (wave_on) {
+  if (wave_on && h) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int r = 32 * b + l32;
@@ -180,11 +181,10 @@ __global__ __launch_bounds__(kThreads) void g1_kernel(const uint16_t* __restrict
 // G2: y[p][n] = w_p * (down_n . h_p) in fp32.  Wave w: output columns
 // ncol = n0 + 64w .. +64 (two 32-row MFMA blocks).
 // ---------------------------------------------------------------------------
-// Y: float (fp32 y) or uint16_t (y rounded to bf16).
-template <int FMT, int NB, typename Y>
+template <int FMT, int NB>
 __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_t* h, int H, int I, int ncol,
                                         bool on, const uint8_t* q0, const SRow<FMT>& s0, const uint8_t* q1,
-                                        const SRow<FMT>& s1, int row0, int nrows, Y* __restrict__ y) {
+                                        const SRow<FMT>& s1, int row0, int nrows, uint16_t* __restrict__ y) {
   using C = Core<FMT, NB>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t roff[C::kInstr];  // byte offset of each staged h row (relative to the tile's first row)
@@ -202,76 +202,41 @@ __device__ __forceinline__ void g2_tile(char* sX, const float* sw, const uint16_
   C::run(sX, C::kBufBytes, reinterpret_cast<const char*>(h + (int64_t)row0 * I), roff, I, q0, s0, q1, s1, on,
          acc0, acc1);
   const int l32 = lane & 31, hh = lane >> 5;
-  if constexpr (sizeof(Y) == 2) {
-    // bf16 y through LDS, so that global stores write whole rows (a direct
-    // store from the MFMA layout touches 32 rows per instruction)
-    constexpr int kPitch = 2 * kG2Rows + 16;  // bytes per staged row (16-B aligned, 8-B writes 2-way at most)
-    static_assert(32 * NB * kPitch <= Lds<FMT>::kG2, "y tile fits the LDS array");
-    __builtin_amdgcn_s_waitcnt(0);  // token DMAs of the extra prefetched step may still be landing
-    __syncthreads();
-    if (on) {
+  // bf16 y through LDS, so that global stores write whole rows (a direct
+  // store from the MFMA layout touches 32 rows per instruction)
+  constexpr int kPitch = 2 * kG2Rows + 16;  // bytes per staged row (16-B aligned, 8-B writes 2-way at most)
+  static_assert(32 * NB * kPitch <= Lds<FMT>::kG2, "y tile fits the LDS array");
+  __builtin_amdgcn_s_waitcnt(0);  // token DMAs of the extra prefetched step may still be landing
+  __syncthreads();
+  if (on) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float wr = sw[32 * b + l32];
-        char* rowp = sX + (32 * b + l32) * kPitch + 2 * (64 * wave + 4 * hh);
+    for (int b = 0; b < NB; ++b) {
+      const float wr = sw[32 * b + l32];
+      char* rowp = sX + (32 * b + l32) * kPitch + 2 * (64 * wave + 4 * hh);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const f32x16& a = m ? acc1[b] : acc0[b];
-            *reinterpret_cast<uint2*>(rowp + 2 * (32 * m + 8 * q)) =
-                make_uint2(pack_bf16x2(a[4 * q] * wr, a[4 * q + 1] * wr), pack_bf16x2(a[4 * q + 2] * wr, a[4 * q + 3] * wr));
-          }
+        for (int m = 0; m < 2; ++m) {
+          const f32x16& a = m ? acc1[b] : acc0[b];
+          *reinterpret_cast<uint2*>(rowp + 2 * (32 * m + 8 * q)) =
+              make_uint2(pack_bf16x2(a[4 * q] * wr, a[4 * q + 1] * wr), pack_bf16x2(a[4 * q + 2] * wr, a[4 * q + 3] * wr));
         }
       }
-    }
-    __syncthreads();
-    const int n0 = ncol - 64 * wave;
-    copy_rows<uint16_t, kBM, 2 * kG2Rows / 16, kPitch>(sX, nrows, H - n0,
-                                                      reinterpret_cast<uint16_t*>(y) + (int64_t)row0 * H + n0, H);
-    return;
-  } else {
-    // fp32 y (the backward's unweighted z) the same way, 128 rows per round
-    constexpr int kPitch = 4 * kG2Rows + 16;
-    constexpr int kRound = 4;  // token blocks per round
-    static_assert(32 * kRound * kPitch <= Lds<FMT>::kG2, "y rows fit the LDS array");
-    const int n0 = ncol - 64 * wave;
-    __builtin_amdgcn_s_waitcnt(0);  // token DMAs of the extra prefetched step may still be landing
-#pragma unroll
-    for (int b0 = 0; b0 < NB; b0 += kRound) {
-      __syncthreads();  // the LDS is free (token buffers, or the previous round's rows)
-      if (on) {
-#pragma unroll
-        for (int b = b0; b < (b0 + kRound < NB ? b0 + kRound : NB); ++b) {
-          const float wr = sw[32 * b + l32];
-          char* rowp = sX + (32 * (b - b0) + l32) * kPitch + 4 * (64 * wave + 4 * hh);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              const f32x16& a = m ? acc1[b] : acc0[b];
-              *reinterpret_cast<float4*>(rowp + 4 * (32 * m + 8 * q)) =
-                  make_float4(a[4 * q] * wr, a[4 * q + 1] * wr, a[4 * q + 2] * wr, a[4 * q + 3] * wr);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      const int rows = nrows - 32 * b0;
-      copy_rows<float, 32 * kRound, 4 * kG2Rows / 16, kPitch>(sX, rows < 32 * kRound ? rows : 32 * kRound, H - n0,
-                                                              reinterpret_cast<float*>(y) + (int64_t)(row0 + 32 * b0) * H + n0, H);
     }
   }
+  __syncthreads();
+  const int n0 = ncol - 64 * wave;
+  copy_rows<uint16_t, kBM, 2 * kG2Rows / 16, kPitch>(sX, nrows, H - n0, y + (int64_t)row0 * H + n0, H);
 }
 
-template <int FMT, typename Y>
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict__ h, const float* __restrict__ wts,
                                                      int32_t E, int32_t H, int32_t I,
                                                      const uint8_t* __restrict__ wq, const float* __restrict__ ws,
                                                      const uint8_t* __restrict__ wsc,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
-                                                     const int32_t* __restrict__ perm_idx, Y* __restrict__ y) {
+                                                     const int32_t* __restrict__ perm_idx, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kG2];
   __shared__ float sw[kBM];
 
@@ -280,8 +245,7 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
   int row0, nrows;
   tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
   const int t = threadIdx.x, wave = t >> 6, l32 = t & 31;
-  // wts == nullptr: unit weights (the backward's unweighted y)
-  if (t < kBM) sw[t] = (t < nrows) ? (wts ? wts[perm_idx[row0 + t]] : 1.0f) : 0.0f;
+  if (t < kBM) sw[t] = (t < nrows) ? wts[perm_idx[row0 + t]] : 0.0f;
 
   const int ncol = ct * kG2Rows + 64 * wave;  // H % 64 == 0: a wave is all in or all out
   const bool on = ncol < H;
@@ -293,23 +257,25 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
   const SRow<FMT> s0 = srow_at<FMT>(ws, wsc, e, H, r0, I, 0);
   const SRow<FMT> s1 = srow_at<FMT>(ws, wsc, e, H, r1, I, 0);
   if (nrows > 192)
-    g2_tile<FMT, 8, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 8>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else if (nrows > 128)
-    g2_tile<FMT, 6, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 6>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else if (nrows > 64)
-    g2_tile<FMT, 4, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 4>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
   else
-    g2_tile<FMT, 2, Y>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
+    g2_tile<FMT, 2>(sX, sw, h, H, I, ncol, on, q0, s0, q1, s1, row0, nrows, y);
 }
 
 // ---------------------------------------------------------------------------
 // Backward through the frozen packed experts (gradients with respect to the
 // hidden states and the routing weights; see moeq_experts_backward):
-//   recompute  g, u, h = G1 of the forward (g and u kept in fp32),
-//              z = down h (G2 with unit weights)
-//   BW         grad_w[a] = dout[t] . z[a]
-//   T1         dh = w * down^T dout[t];  dg = dh u s (1 + g (1 - s)),
+//   recompute  g, u = G1 of the forward, kept in fp32 (h is not stored)
+//   T1         v = down^T dout[t];  dh = w * v;  dg = dh u s (1 + g (1 - s)),
 //              du = dh g s  -> dgu = bf16 [dg | du]                 (s = sigmoid(g))
+//              and, per column tile, the share sum_c v_c h_c of
+//              grad_w[a] = dout[t] . (down h) = v . h, with h = bf16(silu(g) u)
+//              formed again from the saved g and u (the forward's bits)
+//   BW         grad_w[a] = sum of T1's shares over the column tiles, in order
 //   T2         dx = gate_up^T dgu  (fp32, one row per sorted assignment)
 //   C1         grad_x[t] = bf16(sum over k in order of dx)
 // T1 and T2 are transposed grouped GEMMs: the contraction runs over the rows
@@ -329,7 +295,8 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 // group points at row L / 4, columns 4 (L % 4) .. +3 of the block, and lane i
 // receives column i of all four rows.
 //   MODE 1: W = down_e (R = H rows, C = I columns); v_p = dout[perm[p] / K];
-//           the epilogue forms dg and du from dh = w_p * acc and the saved g, u.
+//           the epilogue forms dg and du from dh = w_p * acc and the saved g, u,
+//           and the tile's share of grad_w, sum over its columns of acc * h.
 //   MODE 2: W = gate_up_e (R = 2I, C = H); v_p = dgu[p]; out = dx fp32.
 // Waves: wave w owns output columns 64 (w & 1) .. +64 (two 32-column MFMA
 // blocks) of token rows 128 (w >> 1) .. +128 (four 32-row blocks).
@@ -350,7 +317,8 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
                                                         const int32_t* __restrict__ tile_start,
                                                         const int32_t* __restrict__ perm_idx,
                                                         const float* __restrict__ wts,
-                                                        const float* __restrict__ gu_save, void* __restrict__ out) {
+                                                        const float* __restrict__ gu_save, void* __restrict__ out,
+                                                        float* __restrict__ gw_part) {
   // one LDS array: the dequantized W tiles, then the token tiles
   constexpr int kWBytes = kTk * kTpitch, kVBytes = kBM * kTk * 2;
   // (T2 also stages its fp32 output tile here: kBM rows of kTcols floats, padded)
@@ -594,76 +562,81 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     return;
   }
   if constexpr (MODE == 1) {
-    // dh = w * acc through LDS, then the SwiGLU backward row by row: a
-    // thread takes 4 consecutive columns of a row, so the loads of the saved
-    // fp32 g and u and the stores of bf16 dg and du cover whole rows (from
-    // the accumulator layout each such load touched 32 rows).  The same
-    // fp32 operations in the same order as element by element.
+    // acc (= down^T dout, unweighted) through LDS, then row by row: a thread
+    // takes 4 consecutive columns of a row, so the loads of the saved fp32 g
+    // and u and the stores of bf16 dg and du cover whole rows (from the
+    // accumulator layout each such load touched 32 rows).  Per element
+    // dh = w * acc; the row's share of grad_w adds acc * h over the thread's
+    // columns in order, then over the row's 32 lanes in a fixed tree.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float w = sw[tw + 32 * b + l32];
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x16& a = acc[m][b];
           *reinterpret_cast<float4*>(smem + (tw + 32 * b + l32) * kOutPitch + 4 * (cw + 32 * m + 8 * q + 4 * hh)) =
-              make_float4(w * a[4 * q], w * a[4 * q + 1], w * a[4 * q + 2], w * a[4 * q + 3]);
+              make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         }
-    }
     __syncthreads();
-    constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row
+    constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row (a row: 32 lanes of one wave)
+    static_assert(kChunks == 32, "one row per half wave");
+    const int nct = (C + kTcols - 1) / kTcols;
 #pragma unroll 4
     for (int u = 0; u < kBM * kChunks / kThreads; ++u) {
       const int i = threadIdx.x + u * kThreads, r = i / kChunks, k4 = i - r * kChunks;
       const int c = c0 + 4 * k4;
+      float share = 0.0f;
       if (r < nrows && c < C) {
         const int64_t p = row0 + r;
-        const float4 d4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
+        const float w = sw[r];
+        const float4 a4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
         const float4 g4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + c);
         const float4 u4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + C + c);
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w},
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w},
                     uv[4] = {u4.x, u4.y, u4.z, u4.w};
-        float dg[4], du[4];
+        float dg[4], du[4], hf[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
-          du[e] = dv[e] * gv[e] * sg;
-          dg[e] = dv[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+          const float dv = w * av[e];
+          du[e] = dv * gv[e] * sg;
+          dg[e] = dv * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+          hf[e] = gv[e] * uv[e] * sg;  // the forward's h before rounding, same operations
         }
+        const uint32_t h01 = pack_bf16x2(hf[0], hf[1]), h23 = pack_bf16x2(hf[2], hf[3]);
+        const float hv[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u),
+                             __uint_as_float(h23 << 16), __uint_as_float(h23 & 0xffff0000u)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) share += av[e] * hv[e];
         uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
         *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
         *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
       }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) share += __shfl_xor(share, o, 64);
+      if (k4 == 0 && r < nrows) gw_part[(int64_t)(row0 + r) * nct + ct] = share;
     }
     return;
   }
   static_assert(MODE == 1 || MODE == 2, "T1 or T2");
 }
 
-// grad_w[a] = dout[a / K] . z[slot[a]] (0 for an unrouted assignment), one
-// wave per assignment, lanes summed in a fixed tree order.
-__global__ __launch_bounds__(kThreads) void gradw_kernel(const uint16_t* __restrict__ dout,
-                                                        const float* __restrict__ z,
-                                                        const int32_t* __restrict__ slot, int32_t n, int32_t K,
-                                                        int32_t H, float* __restrict__ gw) {
+// grad_w[a] = sum over the column tiles ct = 0, 1, ... of T1's shares
+// gw_part[slot[a]][ct] (0 for an unrouted assignment), one wave per
+// assignment, lanes summed in a fixed tree order.
+__global__ __launch_bounds__(kThreads) void gradw_kernel(const float* __restrict__ gw_part,
+                                                        const int32_t* __restrict__ slot, int32_t n, int32_t nct,
+                                                        float* __restrict__ gw) {
   const int64_t a = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (a >= n) return;
   const int lane = threadIdx.x & 63;
   const int p = slot[a];
   float acc = 0.0f;
-  if (p >= 0) {
-    const uint16_t* d = dout + (a / K) * H;
-    const float* zr = z + (int64_t)p * H;
-    for (int j = 4 * lane; j < H; j += 256) {
-      const uint2 dv = *reinterpret_cast<const uint2*>(d + j);
-      const float4 zv = *reinterpret_cast<const float4*>(zr + j);
-      acc += __uint_as_float(dv.x << 16) * zv.x + __uint_as_float(dv.x & 0xffff0000u) * zv.y +
-             __uint_as_float(dv.y << 16) * zv.z + __uint_as_float(dv.y & 0xffff0000u) * zv.w;
-    }
-  }
+  if (p >= 0)
+    for (int j = lane; j < nct; j += 64) acc += gw_part[(int64_t)p * nct + j];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (lane == 0) gw[a] = acc;
@@ -673,6 +646,8 @@ __global__ __launch_bounds__(kThreads) void gradw_kernel(const uint16_t* __restr
 }  // namespace
 
 int32_t forward_tile_rows() { return kBM; }
+
+int32_t backward_col_tiles(int32_t I) { return (I + kTcols - 1) / kTcols; }
 
 template <int FMT>
 hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
@@ -692,7 +667,7 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
   if (ev) (void)hipEventRecord(ev[2], s);
   // y rows rounded to bf16 here (the fp32 workspace buffer holds them)
   uint16_t* y16 = reinterpret_cast<uint16_t*>(a.y);
-  g2_kernel<FMT, uint16_t><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
+  g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
                                                    a.rb.tile_start, a.rb.perm, y16);
   if (ev) (void)hipEventRecord(ev[3], s);
   combine_kernel<uint16_t><<<a.T, kThreads, 0, s>>>(y16, a.rb.slot, a.K, a.H, a.out);
@@ -713,22 +688,20 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int mtiles = (n + kBM - 1) / kBM + a.E;
   const int g1 = round_up(mtiles * ((a.I + kG1Cols - 1) / kG1Cols), kXcds);
-  const int g2 = round_up(mtiles * ((a.H + kG2Rows - 1) / kG2Rows), kXcds);
   const int t1 = round_up(mtiles * ((a.I + kTcols - 1) / kTcols), kXcds);
   const int t2 = round_up(mtiles * ((a.H + kTcols - 1) / kTcols), kXcds);
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   const RouteBuffers& r = a.rb;
   g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, r.offsets, r.tile_start,
-                                         r.perm, a.h, a.gu_save);
-  g2_kernel<FMT, float><<<g2, kThreads, 0, s>>>(a.h, nullptr, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
-                                                r.tile_start, r.perm, a.zdx);
-  gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.dout, a.zdx, r.slot, n, a.K, a.H, a.grad_w);
+                                         r.perm, nullptr, a.gu_save);
   tgemm_kernel<FMT, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
-                                               r.tile_start, r.perm, a.wts, a.gu_save, a.dgu);
+                                               r.tile_start, r.perm, a.wts, a.gu_save, a.dgu, a.gw_part);
+  gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.gw_part, r.slot, n, backward_col_tiles(a.I),
+                                                              a.grad_w);
   tgemm_kernel<FMT, 2><<<t2, kThreads, 0, s>>>(a.dgu, a.K, a.E, 2 * a.I, a.H, guq, a.gu_s, a.gu_c, r.offsets,
-                                               r.tile_start, r.perm, nullptr, nullptr, a.zdx);
-  combine_kernel<float><<<a.T, kThreads, 0, s>>>(a.zdx, r.slot, a.K, a.H, a.grad_x);
+                                               r.tile_start, r.perm, nullptr, nullptr, a.dx, nullptr);
+  combine_kernel<float><<<a.T, kThreads, 0, s>>>(a.dx, r.slot, a.K, a.H, a.grad_x);
   return hipGetLastError();
 }
 

@@ -139,9 +139,9 @@ struct BackwardArgs {
   uint16_t* grad_x;         // [T][H]
   float* grad_w;            // [T][K]
   RouteBuffers rb;
-  uint16_t* h;              // [n][I] bf16, sorted rows
+  float* gw_part;           // [n][backward_col_tiles(I)] fp32, sorted rows: T1's shares of grad_w
   float* gu_save;           // [n][2I] fp32, sorted rows
-  float* zdx;               // [n][H] fp32, sorted rows: z, then dx
+  float* dx;                // [n][H] fp32, sorted rows
   uint16_t* dgu;            // [n][2I] bf16, sorted rows
 };
 hipError_t launch_experts_backward(const BackwardArgs& a, hipStream_t s);
@@ -154,5 +154,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int
                          int32_t renorm, int32_t* idx, float* wts, int32_t* rank, int32_t* chunk_counts,
                          hipStream_t s);
 int32_t forward_tile_rows();
+// column tiles of the backward's T1 over I columns (grad_w shares per row)
+int32_t backward_col_tiles(int32_t I);
 
 }  // namespace moeq

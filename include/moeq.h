@@ -254,8 +254,9 @@ moeq_status moeq_experts_forward_noalloc(const uint16_t *hidden_bf16, const int3
  *                      added in k order, with dh = w * down^T grad_out_t,
  *                      dg = dh u s (1 + g (1 - s)), du = dh g s,
  *                      s = sigmoid(g), g / u the gate / up projections
- *   grad_weights       fp32 [T][K]: dL/dw[t,k] = grad_out_t . (down h);
- *                      0 for an unrouted assignment
+ *   grad_weights       fp32 [T][K]: dL/dw[t,k] = grad_out_t . (down h),
+ *                      formed as (down^T grad_out_t) . h from the down^T
+ *                      product that dh needs; 0 for an unrouted assignment
  * Same arguments and rules as moeq_experts_forward otherwise; the forward's
  * gate_up GEMM is recomputed inside (g, u and h are not taken from a previous
  * call).  Roundings: h and dg/du feed bf16 MFMA operands; every sum is fp32;

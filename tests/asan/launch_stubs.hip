@@ -42,6 +42,7 @@ hipError_t launch_router(const uint16_t*, const uint16_t*, int32_t, int32_t, int
   return hit();
 }
 int32_t forward_tile_rows() { return 256; }
+int32_t backward_col_tiles(int32_t I) { return (I + 127) / 128; }
 // The workspace carve-up only needs a count here (the driver checks errors,
 // not sizes): one slice of y.
 int decode_down_splits(int64_t, int32_t, int64_t, int64_t) { return 1; }
