@@ -303,9 +303,7 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 constexpr int kTcols = 128;               // output columns per tile
 constexpr int kTk = 64;                   // weight rows per K step
-// LDS bytes per dequantized W row: 64 B past 256, so the four rows that
-// one transposed read spans (64 B of each) fall on distinct banks.
-constexpr int kTpitch = 2 * kTcols + 64;
+constexpr int kTpitch = 2 * kTcols + 32;  // LDS bytes per dequantized W row (padded)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -385,10 +383,6 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     Dequant<MOEQ_FMT_INT8_ROWWISE> d8;
   };
   constexpr int kWItems = kNf4Codes<FMT> ? 4 + 4 * 5 : 1 + 4 * 3;
-  // A thread stores its four 16-B fragments in the order rot, rot + 1, ...
-  // (mod 4), rot = wr % 4: the 16 lanes of one store then cover 16 distinct
-  // 16-B bank groups.
-  const int rot = wr & 3;
   auto witem = [&](int j, const WCodes& c, WStage& w, int buf) {
     char* dst = sW(buf) + wr * kTpitch + 64 * (t & 3);
     if constexpr (kNf4Codes<FMT>) {
@@ -404,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
         w.tb.hi[j] = perm(p1, p0, 0x07050301u);
         pin_out(w.tb.lo[j]), pin_out(w.tb.hi[j]);
       } else {
-        const int f = (((j - 4) / 5) + rot) & 3, k = (j - 4) % 5;
+        const int f = (j - 4) / 5, k = (j - 4) % 5;
         if (k < 4) {
           if (k == 0) w.f4.w = f == 0 ? c.a.x : (f == 1 ? c.a.y : (f == 2 ? c.a.z : c.a.w));
           w.f4.stage(k, w.tb);
@@ -417,10 +411,10 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
         w.d8.s = c.s.masked(c.m).value();
         w.d8.ns128 = -128.0f * w.d8.s;
       } else {
-        const int f = (((j - 1) / 3) + rot) & 3, k = (j - 1) % 3;
+        const int f = (j - 1) / 3, k = (j - 1) % 3;
         if (k < 2) {
           if (k == 0) {
-            const uint4 q = f < 2 ? c.a : c.b;
+            const uint4& q = f < 2 ? c.a : c.b;
             w.f8.w[0] = (f & 1) ? q.z : q.x;
             w.f8.w[1] = (f & 1) ? q.w : q.y;
           }
