@@ -109,12 +109,17 @@ def test_backward_edge_routing(fmt):
     idx[5] = [4, 4, 4]
     idx[6] = [-1, s.E, 77]                                          # a token routed nowhere
     wts = rng.uniform(-1, 1, (T, 3)).astype(np.float32)
+    # zero weights: their hidden-state contribution vanishes, but dL/dw is
+    # still dout . (down h), taken from the unweighted down^T product
+    wts[7:17, 1] = 0.0
+    idx[7:17, 1] = np.arange(10) % s.E
     idx_d, wts_d = torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda()
     say(f"backward edge routing fmt={fmt}")
     gx, gw = moeq.moeq_experts_backward(x, idx_d, wts_d, qg, qd, dout)
     torch.cuda.synchronize()
     _compare(x, idx_d, wts_d, gu, dn, dout, fmt, gx, gw, np.arange(T), f"edge {fmt}")
     assert torch.count_nonzero(gx[6]) == 0
+    assert bool((host(gw)[7:17, 1] != 0.0).all()), "zero routing weights still have a weight gradient"
 
 
 def test_backward_is_bit_identical_and_empty_batch():
