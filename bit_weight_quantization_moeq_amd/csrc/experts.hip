@@ -236,14 +236,26 @@ __global__ __launch_bounds__(kThreads) void g2_kernel(const uint16_t* __restrict
                                                      const uint8_t* __restrict__ wsc,
                                                      const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ tile_start,
-                                                     const int32_t* __restrict__ perm_idx, uint16_t* __restrict__ y) {
+                                                     const int32_t* __restrict__ perm_idx, uint16_t* __restrict__ y,
+                                                     int32_t split) {
   __shared__ __attribute__((aligned(16))) char sX[Lds<FMT>::kG2];
   __shared__ float sw[kBM];
 
-  int e, mt, ct;
-  if (!decode_work(tile_start, E, (H + kG2Rows - 1) / kG2Rows, e, mt, ct)) return;
+  // split: each token tile's rows in this many balanced parts, one work item
+  // each (the parts of a column tile next to each other); an output element
+  // is still summed by one wave in the same K order, so the bits do not
+  // depend on the split
+  int e, mt, ct2;
+  if (!decode_work(tile_start, E, split * ((H + kG2Rows - 1) / kG2Rows), e, mt, ct2)) return;
+  const int ct = ct2 / split, part = ct2 - ct * split;
   int row0, nrows;
   tile_rows(offsets, tile_start, e, mt, &row0, &nrows);
+  {
+    const int lo = nrows * part / split, hi = nrows * (part + 1) / split;
+    row0 += lo;
+    nrows = hi - lo;
+  }
+  if (nrows <= 0) return;  // a one-row tile's empty part (every wave leaves, before any barrier)
   const int t = threadIdx.x, wave = t >> 6, l32 = t & 31;
   if (t < kBM) sw[t] = (t < nrows) ? wts[perm_idx[row0 + t]] : 0.0f;
 
@@ -647,6 +659,8 @@ __global__ __launch_bounds__(kThreads) void gradw_kernel(const float* __restrict
 
 }  // namespace
 
+constexpr int kCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
+
 int32_t forward_tile_rows() { return kBM; }
 
 int32_t backward_col_tiles(int32_t I) { return (I + kTcols - 1) / kTcols; }
@@ -661,7 +675,13 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
   // upper bound on the number of token tiles: sum_e ceil(count_e / kBM)
   const int mtiles = (n + kBM - 1) / kBM + a.E;
   const int g1 = round_up(mtiles * ((a.I + kG1Cols - 1) / kG1Cols), kXcds);
-  const int g2 = round_up(mtiles * ((a.H + kG2Rows - 1) / kG2Rows), kXcds);
+  // The down GEMM has few work items when every expert holds one token tile
+  // (prefill of a few hundred tokens over few, wide experts): at most one per
+  // CU even at the upper bound on token tiles.  Its tiles' rows are then
+  // split in two, so the chip fills (the same bits).
+  const int g2cols = (a.H + kG2Rows - 1) / kG2Rows;
+  const int g2split = mtiles * g2cols <= kCUs ? 2 : 1;
+  const int g2 = round_up(mtiles * g2cols * g2split, kXcds);
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, a.rb.offsets,
@@ -670,7 +690,7 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
   // y rows rounded to bf16 here (the fp32 workspace buffer holds them)
   uint16_t* y16 = reinterpret_cast<uint16_t*>(a.y);
   g2_kernel<FMT><<<g2, kThreads, 0, s>>>(a.h, a.wts, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, a.rb.offsets,
-                                                   a.rb.tile_start, a.rb.perm, y16);
+                                                   a.rb.tile_start, a.rb.perm, y16, g2split);
   if (ev) (void)hipEventRecord(ev[3], s);
   combine_kernel<uint16_t><<<a.T, kThreads, 0, s>>>(y16, a.rb.slot, a.K, a.H, a.out);
   if (ev) (void)hipEventRecord(ev[4], s);

@@ -114,6 +114,25 @@ def test_forward_down_split_full(fmt, T):
     _compare(x, idx, wts, gu, dn, fmt, out, np.arange(T), label=f"down split {fmt} T={T}")
 
 
+# The down GEMM splits each token tile's rows in two when it has at most one
+# work item per CU even at the upper bound on token tiles (E = 8 wide experts
+# and 600 tokens here: 12 tiles x 16 column tiles); with 4096 tokens it does
+# not.  An output element keeps one writer and one K order, so the tokens of
+# the small batch come out bit-identical inside the large one; the split batch
+# also meets the oracle.
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+def test_forward_down_row_split_keeps_bits(fmt):
+    s = syn.MoEShape("wide", E=8, H=4096, I=256, K=2, fmt=fmt)
+    gu, dn, x, idx, wts = (t.cuda() for t in syn.layer_inputs(s, 4096, device="cpu"))
+    qg, qd = _quantize(gu, fmt), _quantize(dn, fmt)
+    say(f"forward down row split fmt={fmt}")
+    small = moeq.moeq_experts_forward(x[:600].contiguous(), idx[:600].contiguous(), wts[:600].contiguous(), qg, qd)
+    large = moeq.moeq_experts_forward(x, idx, wts, qg, qd)
+    torch.cuda.synchronize()
+    assert torch.equal(small, large[:600])
+    _compare(x, idx, wts, gu, dn, fmt, small, np.arange(0, 600, 9), label=f"down row split {fmt}")
+
+
 # The path boundary: T*K = 512 is the last few-assignment batch, 514 the
 # first tiled one; every output element of both is checked.
 @pytest.mark.parametrize("T", [256, 257])
