@@ -18,7 +18,12 @@ namespace {
 // no token tiles.  A workgroup owns one touched expert (its blockIdx.x-th, in
 // expert order) and RB row blocks of 64 weight rows; it finds the expert and
 // the expert's assignments itself from top_k_index (ascending assignment
-// order).  Its NW waves are RB row blocks x P parts of K (NW = RB * P, P
+// order).  The assignments go in groups of 32 (one MFMA's columns).  In a
+// batch of more than 32 tokens an expert can hold several groups (skewed
+// routing); then that workgroup takes the first group only, and the grid
+// carries T*K/32 more workgroups (an upper bound on the later groups of all
+// experts), the i-th of which takes the i-th later group in expert order, so
+// the groups run side by side instead of one after the other.  Its NW waves are RB row blocks x P parts of K (NW = RB * P, P
 // chosen on the host so that few touched experts still fill the chip).  Each
 // wave streams its part of its 64 rows' packed codes straight from HBM,
 // dequantizes them in registers into the MFMA A operand and multiplies the
@@ -45,12 +50,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
                                                         const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ ws,
                                                         const uint8_t* __restrict__ wsc,
-                                                        uint16_t* __restrict__ hout, float* __restrict__ yout) {
+                                                        uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                        int32_t nmain) {
   constexpr int kT = NW * 64;
   constexpr int kJ = kDecodeMax / kT;  // assignments per thread
   constexpr int kStep = Fmt<FMT>::kStep;
   constexpr int kS = kStep / 16;
   __shared__ uint32_t bits[MOEQ_MAX_EXPERTS / 32];
+  __shared__ int ecnt[MOEQ_MAX_EXPERTS];  // assignments per expert (later-group workgroups only)
   __shared__ int list[kDecodeMax];
   __shared__ int cnt[kDecodeMax / 64];
   __shared__ float red[NW][2][16][64];
@@ -73,9 +80,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
     if (my[j] >= 0 && my[j] < E) atomicOr(&bits[my[j] >> 5], 1u << (my[j] & 31));
   lds_barrier();
 
-  // 2. this block's expert: the blockIdx.x-th touched one (every wave finds it)
-  int e = -1;
-  {
+  // 2. this block's expert: the blockIdx.x-th touched one (every wave finds
+  //    it), and its first token group; or, for blockIdx.x >= nmain, the
+  //    (blockIdx.x - nmain)-th later group (groups 1, 2, ... of the experts
+  //    holding more than 32 assignments, in expert order)
+  int e = -1, gfirst = 0;
+  const int xb = (int)blockIdx.x - nmain;
+  if (xb < 0) {
     const int nw = (E + 31) / 32;
     const uint32_t wbits = (lane < nw) ? bits[lane] : 0u;
     const int c = __popc(wbits);
@@ -94,6 +105,46 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       e = src * 32 + __builtin_ctz(wb);
     }
     e = __builtin_amdgcn_readfirstlane(e);
+  } else {
+    for (int i = t; i < E; i += kT) ecnt[i] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (my[j] >= 0 && my[j] < E) atomicAdd(&ecnt[my[j]], 1);
+    lds_barrier();
+    // lane l covers experts 16 l .. 16 l + 15 (E <= 1024): its later groups,
+    // then an inclusive scan over the lanes
+    constexpr int kPer = MOEQ_MAX_EXPERTS / 64;
+    int loc = 0;
+    for (int i = 0; i < kPer; ++i) {
+      const int ex = kPer * lane + i;
+      const int c = ex < E ? ecnt[ex] : 0;
+      loc += c > 32 ? (c - 1) / 32 : 0;
+    }
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    const uint64_t who = __ballot((inc - loc) <= xb && xb < inc);
+    if (who) {
+      const int src = __builtin_ctzll(who);
+      int r = xb - (__shfl(inc, src, 64) - __shfl(loc, src, 64));  // rank within the lane's experts
+      for (int i = 0; i < kPer; ++i) {
+        const int ex = kPer * src + i;
+        const int c = ex < E ? ecnt[ex] : 0;
+        const int ng = c > 32 ? (c - 1) / 32 : 0;
+        if (r < ng) {
+          e = ex;
+          gfirst = 32 * (1 + r);
+          break;
+        }
+        r -= ng;
+      }
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    gfirst = __builtin_amdgcn_readfirstlane(gfirst);
   }
   if (e < 0) return;  // the whole block: the bitmap is shared
 
@@ -177,9 +228,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
       c1.fetch(q1, s1, ks * kStep, hh, K, ks < ks1, rs1);
     }
   };
-  fetch_step(ca0, ca1, ks0);
-  fetch_pair(ks0);
-  fetch_oct(ks0);
+  if (gfirst == 0) {  // a later group's workgroup fetches in the group loop
+    fetch_step(ca0, ca1, ks0);
+    fetch_pair(ks0);
+    fetch_oct(ks0);
+  }
 
   // 4. the expert's assignments in ascending order: chunk c = a / 64 is
   //    wave c % NW's j = c / NW values
@@ -201,11 +254,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
   }
   lds_barrier();
 
-  for (int g = 0; g < ne; g += 32) {
+  // one group per workgroup when later groups have their own workgroups
+  const int gend = (int)gridDim.x > nmain ? min(ne, gfirst + 32) : ne;
+  for (int g = gfirst; g < gend; g += 32) {
     const int tok = g + l32 < ne ? g + l32 : g;  // lanes past the tokens repeat one (never stored)
     const int a = list[tok];
     const uint16_t* brow = G1 ? act + (int64_t)(a / Ktop) * H : act + (int64_t)a * I;
-    if (g > 0) {
+    if (g > 0) {  // not prefetched above
       fetch_step(ca0, ca1, ks0);
       fetch_pair(ks0);
       fetch_oct(ks0);
@@ -458,16 +513,19 @@ void launch_decode_gemm(const ForwardArgs& a, int ux, const uint16_t* act, const
   int ab = 0;
   if constexpr (FMT == MOEQ_FMT_NF4)
     ab = (Kr % 1024 == 0 && (Kr / 128) % (8 * pz) == 0) ? 8 : ((Kr / kNf4Block) % 2 == 0 ? 2 : 0);
-  const dim3 grid(ux, d.gy, z);
+  // an expert holds at most T assignments, so more than one group of 32 only
+  // when T > 32: then n / 32 more workgroups take the later groups
+  const int extra = a.T > 32 ? n / 32 : 0;
+  const dim3 grid(ux + extra, d.gy, z);
   if (ab == 8)
     decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 8 : 0><<<grid, kThreads, 0, s>>>(
-        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y, ux);
   else if (ab == 2)
     decode_kernel<FMT, G1, kWaves, FMT == MOEQ_FMT_NF4 ? 2 : 0><<<grid, kThreads, 0, s>>>(
-        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y, ux);
   else
     decode_kernel<FMT, G1, kWaves, 0><<<grid, kThreads, 0, s>>>(
-        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y);
+        act, a.idx, a.wts, n, a.K, a.E, a.H, a.I, d.p, q, sc, scc, a.h, a.y, ux);
 }
 
 template <int FMT>
