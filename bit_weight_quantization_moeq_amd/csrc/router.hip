@@ -79,6 +79,124 @@ __device__ __forceinline__ float unord(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
+// Softmax and top-K by radix select, for E <= 64 NPL with small NPL: the
+// K-th largest order-preserving key (ord of the logit) is found bit by bit
+// from the top, each bit one compare whose ballot, masked to the remaining
+// candidates, gives a scalar count; keys above it are taken, and of the keys
+// equal to it the lowest expert indices fill the rest.  A taken expert's
+// output slot is its rank among the taken (a larger logit first, equal
+// logits by the lower index): the same selection and order as K rounds of
+// arg-max.  Renormalised weights divide by the sum of the taken
+// probabilities (one wave sum).  Wave w takes tokens w, w + 4, w + 8, w + 12,
+// all four at once (independent chains).
+template <int NPL>
+__device__ __forceinline__ void softmax_topk_radix(const float* slog, int64_t t0, int32_t T, int32_t E, int32_t K,
+                                                   int32_t renorm, int wave, int lane, int32_t* __restrict__ idx,
+                                                   float* __restrict__ wts, int* sel) {
+  constexpr int kTT = kTok / kWaves;  // tokens per wave
+  float v[kTT][NPL], m[kTT], inv[kTT];
+  uint32_t key[kTT][NPL];
+  uint64_t cand[kTT][NPL], take[kTT][NPL];
+  int need[kTT];
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) {
+    const int tt = wave + kWaves * q;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + 64 * j;
+      const bool valid = e < E;
+      v[q][j] = valid ? slog[tt * E + e] : -INFINITY;
+      key[q][j] = ord(v[q][j]);
+      cand[q][j] = __ballot(valid);
+      take[q][j] = 0;
+      lm = fmaxf(lm, v[q][j]);
+    }
+    m[q] = unord(wave_umax(ord(lm)));
+    need[q] = K;
+  }
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) ls += (lane + 64 * j < E) ? __expf(v[q][j] - m[q]) : 0.0f;
+    inv[q] = 1.0f / wave_fsum(ls);
+  }
+  for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+    for (int q = 0; q < kTT; ++q) {
+      uint64_t hi[NPL];
+      int c1 = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        hi[j] = cand[q][j] & __ballot((key[q][j] >> bit) & 1u);
+        c1 += __popcll(hi[j]);
+      }
+      if (c1 >= need[q]) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) cand[q][j] = hi[j];
+      } else {
+        need[q] -= c1;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          take[q][j] |= hi[j];
+          cand[q][j] &= ~hi[j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kTT; ++q) {
+    // keys equal to the K-th largest: the lowest expert indices
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      while (need[q] > 0 && cand[q][j]) {
+        const uint64_t low = cand[q][j] & (~cand[q][j] + 1);
+        take[q][j] |= low;
+        cand[q][j] ^= low;
+        --need[q];
+      }
+    }
+    // rank among the taken
+    int rank[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) rank[j] = 0;
+#pragma unroll
+    for (int jj = 0; jj < NPL; ++jj) {
+      for (uint64_t b = take[q][jj]; b; b &= b - 1) {
+        const int l = __builtin_ctzll(b);
+        const uint32_t k2 = __builtin_amdgcn_readlane(key[q][jj], l);
+        const int e2 = l + 64 * jj;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const int e = lane + 64 * j;
+          rank[j] += (k2 > key[q][j] || (k2 == key[q][j] && e2 < e)) ? 1 : 0;
+        }
+      }
+    }
+    float ex[NPL];
+    float ps = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const bool mine = (take[q][j] >> lane) & 1u;
+      ex[j] = mine ? __expf(v[q][j] - m[q]) : 0.0f;
+      ps += ex[j] * inv[q];
+    }
+    const float sel_sum = renorm ? wave_fsum(ps) : 1.0f;
+    const int tt = wave + kWaves * q;
+    const int64_t tok = t0 + tt;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      if (((take[q][j] >> lane) & 1u) && tok < T) {
+        const int e = lane + 64 * j;
+        idx[tok * K + rank[j]] = e;
+        wts[tok * K + rank[j]] = ex[j] * (inv[q] / sel_sum);
+        if (sel) sel[tt * K + rank[j]] = e;
+      }
+    }
+  }
+}
+
 // Softmax over the E logits of each of the block's tokens and the K rounds of
 // arg-max, from the logits in LDS; NPL logits per lane (E <= 64 NPL).
 // sel (LDS, or nullptr): the selections again, sel[tt * K + k] for the
@@ -304,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
 
   int* sl = rank ? sel : nullptr;
   switch ((E + 63) / 64) {
-    case 1: softmax_topk<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
-    case 2: softmax_topk<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 1: softmax_topk_radix<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 2: softmax_topk_radix<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
     case 3:
     case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
     case 5:
