@@ -327,6 +327,61 @@ __device__ __forceinline__ void chunk_rank(const int* sel, int m, int32_t E, int
 
 constexpr int kMaxSel = kTok * kRouterRankMaxK;  // assignments per workgroup when ranking
 
+// The logits' way out, shared by both forms of the logits GEMM: lane holds,
+// per expert block j of the wave, partial logits of experts
+// 32 (g0 + gstep j) + 8 q + 4 hh + i for token l32 over part `part` of H.
+// The parts meet in LDS (added in part order), then softmax and top-K, then
+// (rank != nullptr) the routing stage's rank step over the block's chunk.
+template <int RBW>
+__device__ __forceinline__ void router_tail(const f32x16 (&acc)[RBW], float* slog, int* sel, int64_t t0, int32_t T,
+                                            int32_t E, int32_t K, int32_t renorm, int32_t P, int part, int g0,
+                                            int gstep, int wave, int lane, int32_t* __restrict__ idx,
+                                            float* __restrict__ wts, int32_t* __restrict__ rank,
+                                            int32_t* __restrict__ chunk_counts) {
+  const int t = threadIdx.x, l32 = lane & 31, hh = lane >> 5;
+  if (l32 < kTok) {
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 32 * (g0 + gstep * j) + 8 * q + 4 * hh + i;
+          if (e < E) slog[(part * kTok + l32) * E + e] = acc[j][4 * q + i];
+        }
+    }
+  }
+  __syncthreads();
+  if (P > 1) {  // add the parts in part order into part 0
+    for (int i = t; i < kTok * E; i += kThreads) {
+      float v = slog[i];
+      for (int p = 1; p < P; ++p) v += slog[p * kTok * E + i];
+      slog[i] = v;
+    }
+    __syncthreads();
+  }
+
+  int* sl = rank ? sel : nullptr;
+  switch ((E + 63) / 64) {
+    case 1: softmax_topk_radix<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 2: softmax_topk_radix<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 3:
+    case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    case 5:
+    case 6:
+    case 7:
+    case 8: softmax_topk<8>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+    default: softmax_topk<(MOEQ_MAX_EXPERTS + 63) / 64>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+  }
+  if (rank) {
+    // the logits are no longer needed: their LDS holds the rank counters
+    // (4 E + E ints <= kTok E floats)
+    __syncthreads();
+    const int ntok = (int)min<int64_t>(kTok, T - t0);
+    chunk_rank(sel, ntok * K, E, reinterpret_cast<int*>(slog), t0 * K, rank, chunk_counts + (int64_t)blockIdx.x * E);
+  }
+}
+
 // rank / chunk_counts: nullptr, or the routing stage's rank [T*K] and
 // chunk_counts [ceil(T/16)][E] (chunks of 16 tokens x K assignments).
 template <int RBW>  // expert blocks of 32 per wave
@@ -397,48 +452,106 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     __builtin_amdgcn_sched_barrier(0);
   }
   if (i < n64) mul(fa);  // odd trip count: the last trip, already loaded
-  // lane holds partial logits of experts 32 (g0 + gstep j) + 8 q + 4 hh + i for token l32
-  if (l32 < kTok) {
-#pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 32 * (g0 + gstep * j) + 8 * q + 4 * hh + i;
-          if (e < E) slog[(part * kTok + l32) * E + e] = acc[j][4 * q + i];
-        }
-    }
-  }
-  __syncthreads();
-  if (P > 1) {  // add the parts in part order into part 0
-    for (int i = t; i < kTok * E; i += kThreads) {
-      float v = slog[i];
-      for (int p = 1; p < P; ++p) v += slog[p * kTok * E + i];
-      slog[i] = v;
-    }
-    __syncthreads();
-  }
+  router_tail<RBW>(acc, slog, sel, t0, T, E, K, renorm, P, part, g0, gstep, wave, lane, idx, wts, rank, chunk_counts);
+}
 
-  int* sl = rank ? sel : nullptr;
-  switch ((E + 63) / 64) {
-    case 1: softmax_topk_radix<1>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
-    case 2: softmax_topk_radix<2>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
-    case 3:
-    case 4: softmax_topk<4>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
-    case 5:
-    case 6:
-    case 7:
-    case 8: softmax_topk<8>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
-    default: softmax_topk<(MOEQ_MAX_EXPERTS + 63) / 64>(slog, t0, T, E, K, renorm, wave, lane, idx, wts, sl); break;
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4, LDS base in M0), as inline assembly so that the
+// compiler sees no LDS write to order against its own LDS reads: explicit
+// waits before the barriers order the copies.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+// The logits GEMM with its operands staged through LDS, for E <= 32 NRB with
+// NRB expert blocks of 32 and P = 4 / NRB parts of H: wave w takes expert
+// block w / P over part w % P.  Loaded straight into the MFMA layout, each
+// 16-B lane load touches one cache line per row (32 per instruction); here
+// every 64-k trip of the gate rows and the block's token rows is copied into
+// LDS first, 8 whole 128-B row pieces per instruction, double-buffered, and
+// the fragments are read from LDS.  Rows are stored with their 16-B chunks
+// XOR-swizzled by (row / 2) % 8, so a fragment read (32 rows, one chunk)
+// hits distinct banks.  The MFMAs, their operands and the logits' way out
+// are those of router_kernel.
+template <int NRB>
+__global__ __launch_bounds__(kThreads) void router_staged_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ gate, int32_t T,
+                                                                int32_t H, int32_t E, int32_t K, int32_t renorm,
+                                                                int32_t* __restrict__ idx, float* __restrict__ wts,
+                                                                int32_t* __restrict__ rank,
+                                                                int32_t* __restrict__ chunk_counts) {
+  constexpr int P = kWaves / NRB;                    // parts of H
+  static_assert(NRB * P == kWaves, "one expert block and one part of H per wave");
+  constexpr int kRows = 32 * NRB + kTok;             // staged rows per part: gate rows, then token rows
+  constexpr int kPartBytes = kRows * 128;            // 64 k of each row
+  constexpr int kBufBytes = P * kPartBytes;
+  constexpr int kGroups = kRows / 8;                 // 8-row copies per part
+  constexpr int kCopies = P * kGroups;               // per trip
+  constexpr int kCopiesW = (kCopies + kWaves - 1) / kWaves;  // per wave (the last copy repeated to even out)
+  extern __shared__ float slog[];  // [P][kTok][E]: partial logits of the P parts of H
+  __shared__ int sel[kMaxSel];
+  __shared__ __attribute__((aligned(16))) char ring[2 * kBufBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int part = wave % P, g0 = wave / P;
+  const int hlen = H / P;  // H % (64 P) == 0
+  const int n64 = hlen / 64;
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  // this wave's copies: copy d moves rows 8 (d % kGroups) .. +7 of part
+  // d / kGroups; lane l takes row 8 (d % kGroups) + l / 8 and lands in its
+  // LDS slot l % 8, which holds chunk (l % 8) ^ swz(row)
+  const uint16_t* src[kCopiesW];
+  uint32_t dst[kCopiesW];
+#pragma unroll
+  for (int c = 0; c < kCopiesW; ++c) {
+    const int d = min(wave + kWaves * c, kCopies - 1);
+    const int p = d / kGroups, g = d % kGroups, rr = 8 * g + (lane >> 3);
+    const uint16_t* row;
+    if (rr < 32 * NRB) {
+      row = gate + (int64_t)(rr < E ? rr : 0) * H;  // rows past E: row 0 (its logits are never stored)
+    } else {
+      const int64_t tk = t0 + (rr - 32 * NRB);
+      row = x + (tk < T ? tk : t0) * H;  // tokens past T: the block's first (never stored)
+    }
+    src[c] = row + p * hlen + 8 * ((lane & 7) ^ swz(rr));
+    dst[c] = (uint32_t)(p * kPartBytes + g * 8 * 128);
   }
-  if (rank) {
-    // the logits are no longer needed: their LDS holds the rank counters
-    // (4 E + E ints <= kTok E floats)
-    __syncthreads();
-    const int ntok = (int)min<int64_t>(kTok, T - t0);
-    chunk_rank(sel, ntok * K, E, reinterpret_cast<int*>(slog), t0 * K, rank, chunk_counts + (int64_t)blockIdx.x * E);
+  uint32_t rlds = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring;
+  asm volatile("" : "+s"(rlds));  // opaque, so it is not folded back into a pointer to the array
+  auto stage = [&](int trip, int buf) {
+#pragma unroll
+    for (int c = 0; c < kCopiesW; ++c) lds_copy16(src[c] + 64 * trip, rlds + buf * kBufBytes + dst[c]);
+  };
+
+  f32x16 acc[1];
+  acc[0] = (f32x16){};
+  const int arow = 32 * g0 + l32, brow = 32 * NRB + (l32 & (kTok - 1));  // token columns 16..31 repeat 0..15
+  stage(0, 0);
+  for (int i = 0; i < n64; ++i) {
+    if (i + 1 < n64) {
+      stage(i + 1, (i + 1) & 1);
+      __builtin_amdgcn_s_waitcnt((kCopiesW & 0xF) | ((kCopiesW >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's copies of trip i have landed
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const char* base = ring + (i & 1) * kBufBytes + part * kPartBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 2 * u + hh;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + arow * 128 + 16 * (c ^ swz(arow)));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(base + brow * 128 + 16 * (c ^ swz(brow)));
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[0], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4));  // this trip's LDS reads done
+    __builtin_amdgcn_s_barrier();  // before trip i + 2 is copied over buffer i % 2
   }
+  router_tail<1>(acc, slog, sel, t0, T, E, K, renorm, P, part, g0, kWaves, wave, lane, idx, wts, rank, chunk_counts);
 }
 
 }  // namespace
@@ -448,6 +561,18 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* gate, int32_t T, int
                          hipStream_t s) {
   const int grid = (T + kTok - 1) / kTok;
   const int nrb = (E + 31) / 32;  // expert blocks of 32
+  // one, two or four expert blocks: operands staged through LDS (one block
+  // and one part of H per wave)
+  if ((nrb == 1 || nrb == 2 || nrb == 4) && H % (64 * (kWaves / nrb)) == 0) {
+    const size_t lds_st = sizeof(float) * kTok * (size_t)E * (kWaves / nrb);
+    if (nrb == 1)
+      router_staged_kernel<1><<<grid, kThreads, lds_st, s>>>(x, gate, T, H, E, K, renorm, idx, wts, rank, chunk_counts);
+    else if (nrb == 2)
+      router_staged_kernel<2><<<grid, kThreads, lds_st, s>>>(x, gate, T, H, E, K, renorm, idx, wts, rank, chunk_counts);
+    else
+      router_staged_kernel<4><<<grid, kThreads, lds_st, s>>>(x, gate, T, H, E, K, renorm, idx, wts, rank, chunk_counts);
+    return hipGetLastError();
+  }
   // few expert blocks: split H across the waves instead (P parts, H % 64P == 0)
   int P = nrb >= kWaves ? 1 : (nrb >= 2 ? 2 : 4);
   while (P > 1 && H % (64 * P) != 0) P /= 2;
