@@ -469,8 +469,8 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
 // block w / P over part w % P.  Loaded straight into the MFMA layout, each
 // 16-B lane load touches one cache line per row (32 per instruction); here
 // every 64-k trip of the gate rows and the block's token rows is copied into
-// LDS first, 8 whole 128-B row pieces per instruction, double-buffered, and
-// the fragments are read from LDS.  Rows are stored with their 16-B chunks
+// LDS first, 8 whole 128-B row pieces per instruction, two trips ahead
+// through three buffers, and the fragments are read from LDS.  Rows are stored with their 16-B chunks
 // XOR-swizzled by (row / 2) % 8, so a fragment read (32 rows, one chunk)
 // hits distinct banks.  The MFMAs, their operands and the logits' way out
 // are those of router_kernel.
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void router_staged_kernel(const uint16_t*
   constexpr int kCopiesW = (kCopies + kWaves - 1) / kWaves;  // per wave (the last copy repeated to even out)
   extern __shared__ float slog[];  // [P][kTok][E]: partial logits of the P parts of H
   __shared__ int sel[kMaxSel];
-  __shared__ __attribute__((aligned(16))) char ring[2 * kBufBytes];
+  __shared__ __attribute__((aligned(16))) char ring[3 * kBufBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
@@ -531,16 +531,20 @@ __global__ __launch_bounds__(kThreads) void router_staged_kernel(const uint16_t*
   acc[0] = (f32x16){};
   const int arow = 32 * g0 + l32, brow = 32 * NRB + (l32 & (kTok - 1));  // token columns 16..31 repeat 0..15
   stage(0, 0);
+  if (n64 > 1) stage(1, 1);
   for (int i = 0; i < n64; ++i) {
-    if (i + 1 < n64) {
-      stage(i + 1, (i + 1) & 1);
+    if (i + 2 < n64) {
+      stage(i + 2, (i + 2) % 3);
+      constexpr int kW = 2 * kCopiesW;
+      __builtin_amdgcn_s_waitcnt((kW & 0xF) | ((kW >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    } else if (i + 1 < n64) {
       __builtin_amdgcn_s_waitcnt((kCopiesW & 0xF) | ((kCopiesW >> 4) << 14) | (0x7 << 4) | (0xF << 8));
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
     __builtin_amdgcn_s_barrier();  // every wave's copies of trip i have landed
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    const char* base = ring + (i & 1) * kBufBytes + part * kPartBytes;
+    const char* base = ring + (i % 3) * kBufBytes + part * kPartBytes;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = 2 * u + hh;
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void router_staged_kernel(const uint16_t*
       acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[0], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4));  // this trip's LDS reads done
-    __builtin_amdgcn_s_barrier();  // before trip i + 2 is copied over buffer i % 2
+    __builtin_amdgcn_s_barrier();  // before trip i + 3 is copied over buffer i % 3
   }
   router_tail<1>(acc, slog, sel, t0, T, E, K, renorm, P, part, g0, kWaves, wave, lane, idx, wts, rank, chunk_counts);
 }
