@@ -88,89 +88,77 @@ __device__ __forceinline__ float unord(uint32_t u) {
 // logits by the lower index): the same selection and order as K rounds of
 // arg-max.  Renormalised weights divide by the sum of the taken
 // probabilities (one wave sum).  Wave w takes tokens w, w + 4, w + 8, w + 12,
-// all four at once (independent chains).
+// one after the other (four at once measured no faster: their candidate
+// masks spill scalar registers).
 template <int NPL>
 __device__ __forceinline__ void softmax_topk_radix(const float* slog, int64_t t0, int32_t T, int32_t E, int32_t K,
                                                    int32_t renorm, int wave, int lane, int32_t* __restrict__ idx,
                                                    float* __restrict__ wts, int* sel) {
-  constexpr int kTT = kTok / kWaves;  // tokens per wave
-  float v[kTT][NPL], m[kTT], inv[kTT];
-  uint32_t key[kTT][NPL];
-  uint64_t cand[kTT][NPL], take[kTT][NPL];
-  int need[kTT];
-#pragma unroll
+  constexpr int kTT = kTok / kWaves;  // tokens per wave, one after the other
   for (int q = 0; q < kTT; ++q) {
     const int tt = wave + kWaves * q;
+    float v[NPL];
+    uint32_t key[NPL];
+    uint64_t cand[NPL], take[NPL];
     float lm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int e = lane + 64 * j;
       const bool valid = e < E;
-      v[q][j] = valid ? slog[tt * E + e] : -INFINITY;
-      key[q][j] = ord(v[q][j]);
-      cand[q][j] = __ballot(valid);
-      take[q][j] = 0;
-      lm = fmaxf(lm, v[q][j]);
+      v[j] = valid ? slog[tt * E + e] : -INFINITY;
+      key[j] = ord(v[j]);
+      cand[j] = __ballot(valid);
+      take[j] = 0;
+      lm = fmaxf(lm, v[j]);
     }
-    m[q] = unord(wave_umax(ord(lm)));
-    need[q] = K;
-  }
-#pragma unroll
-  for (int q = 0; q < kTT; ++q) {
+    const float m = unord(wave_umax(ord(lm)));
     float ls = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) ls += (lane + 64 * j < E) ? __expf(v[q][j] - m[q]) : 0.0f;
-    inv[q] = 1.0f / wave_fsum(ls);
-  }
-  for (int bit = 31; bit >= 0; --bit) {
-#pragma unroll
-    for (int q = 0; q < kTT; ++q) {
+    for (int j = 0; j < NPL; ++j) ls += (lane + 64 * j < E) ? __expf(v[j] - m) : 0.0f;
+    const float inv = 1.0f / wave_fsum(ls);
+    int need = K;
+    for (int bit = 31; bit >= 0; --bit) {
       uint64_t hi[NPL];
       int c1 = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
-        hi[j] = cand[q][j] & __ballot((key[q][j] >> bit) & 1u);
+        hi[j] = cand[j] & __ballot((key[j] >> bit) & 1u);
         c1 += __popcll(hi[j]);
       }
-      if (c1 >= need[q]) {
+      if (c1 >= need) {
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) cand[q][j] = hi[j];
+        for (int j = 0; j < NPL; ++j) cand[j] = hi[j];
       } else {
-        need[q] -= c1;
+        need -= c1;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-          take[q][j] |= hi[j];
-          cand[q][j] &= ~hi[j];
+          take[j] |= hi[j];
+          cand[j] &= ~hi[j];
         }
       }
     }
-  }
-#pragma unroll
-  for (int q = 0; q < kTT; ++q) {
-    // keys equal to the K-th largest: the lowest expert indices
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      while (need[q] > 0 && cand[q][j]) {
-        const uint64_t low = cand[q][j] & (~cand[q][j] + 1);
-        take[q][j] |= low;
-        cand[q][j] ^= low;
-        --need[q];
+      while (need > 0 && cand[j]) {
+        const uint64_t low = cand[j] & (~cand[j] + 1);
+        take[j] |= low;
+        cand[j] ^= low;
+        --need;
       }
     }
-    // rank among the taken
     int rank[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) rank[j] = 0;
 #pragma unroll
     for (int jj = 0; jj < NPL; ++jj) {
-      for (uint64_t b = take[q][jj]; b; b &= b - 1) {
+      for (uint64_t b = take[jj]; b; b &= b - 1) {
         const int l = __builtin_ctzll(b);
-        const uint32_t k2 = __builtin_amdgcn_readlane(key[q][jj], l);
+        const uint32_t k2 = __builtin_amdgcn_readlane(key[jj], l);
         const int e2 = l + 64 * jj;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
           const int e = lane + 64 * j;
-          rank[j] += (k2 > key[q][j] || (k2 == key[q][j] && e2 < e)) ? 1 : 0;
+          rank[j] += (k2 > key[j] || (k2 == key[j] && e2 < e)) ? 1 : 0;
         }
       }
     }
@@ -178,19 +166,18 @@ __device__ __forceinline__ void softmax_topk_radix(const float* slog, int64_t t0
     float ps = 0.0f;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const bool mine = (take[q][j] >> lane) & 1u;
-      ex[j] = mine ? __expf(v[q][j] - m[q]) : 0.0f;
-      ps += ex[j] * inv[q];
+      const bool mine = (take[j] >> lane) & 1u;
+      ex[j] = mine ? __expf(v[j] - m) : 0.0f;
+      ps += ex[j] * inv;
     }
     const float sel_sum = renorm ? wave_fsum(ps) : 1.0f;
-    const int tt = wave + kWaves * q;
     const int64_t tok = t0 + tt;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      if (((take[q][j] >> lane) & 1u) && tok < T) {
+      if (((take[j] >> lane) & 1u) && tok < T) {
         const int e = lane + 64 * j;
         idx[tok * K + rank[j]] = e;
-        wts[tok * K + rank[j]] = ex[j] * (inv[q] / sel_sum);
+        wts[tok * K + rank[j]] = ex[j] * (inv / sel_sum);
         if (sel) sel[tt * K + rank[j]] = e;
       }
     }
