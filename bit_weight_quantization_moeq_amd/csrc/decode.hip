@@ -426,19 +426,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const uint16_t* __restr
 // Decode combine: out[t] = bf16(sum over k in order of y[t*K + k]), skipping
 // unrouted assignments, where y[a] is the sum over z in order of the Z slices
 // y_z[a] (the down launch's parts of K across workgroups; Z = 1, 2 or 4).
-// One workgroup per token: the routing entries are read once into LDS, then
-// each thread keeps 8 y loads (8 / Z assignments) in flight at once.
+// One workgroup per token; each thread keeps 8 y loads (8 / Z assignments) in
+// flight at once.  y rows are indexed by assignment and lie in the workspace
+// whether or not the assignment is routed, so the loads do not wait for the
+// routing entries (uniform scalar loads, read alongside): an unrouted
+// assignment's row, never written, is loaded and left out of the sum.
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* __restrict__ y,
                                                                  const int32_t* __restrict__ idx, int32_t K,
                                                                  int32_t E, int32_t H, int32_t zlog,
                                                                  int64_t zstride, uint16_t* __restrict__ out) {
-  __shared__ uint8_t routed[kDecodeMax];
   const int64_t tok = blockIdx.x;
-  for (int k = threadIdx.x; k < K; k += kThreads) {
-    const int e = idx[tok * K + k];
-    routed[k] = e >= 0 && e < E;
-  }
-  __syncthreads();
   const int Z = 1 << zlog, kc = 8 >> zlog;
   for (int n4 = threadIdx.x; n4 < H / 4; n4 += kThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -448,9 +445,11 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float* _
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + (u >> zlog), z = u & (Z - 1);
-        use[u] = (u >> zlog) < kc && k < K && routed[k];
-        v[u] = use[u] ? *reinterpret_cast<const float4*>(y + z * zstride + (tok * K + k) * H + 4 * n4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool in = (u >> zlog) < kc && k < K;
+        const int e = in ? idx[tok * K + k] : -1;
+        use[u] = in && e >= 0 && e < E;
+        v[u] = in ? *reinterpret_cast<const float4*>(y + z * zstride + (tok * K + k) * H + 4 * n4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       float4 sk = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
