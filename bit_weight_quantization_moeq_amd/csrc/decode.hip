@@ -23,8 +23,9 @@ namespace {
 // routing); then that workgroup takes the first group only, and the grid
 // carries T*K/32 more workgroups (an upper bound on the later groups of all
 // experts), the i-th of which takes the i-th later group in expert order, so
-// the groups run side by side instead of one after the other.  Its NW waves are RB row blocks x P parts of K (NW = RB * P, P
-// chosen on the host so that few touched experts still fill the chip).  Each
+// the groups run side by side instead of one after the other.  Its NW waves
+// are RB row blocks x P parts of K (NW = RB * P, P chosen on the host so that
+// few touched experts still fill the chip).  Each
 // wave streams its part of its 64 rows' packed codes straight from HBM,
 // dequantizes them in registers into the MFMA A operand and multiplies the
 // expert's token rows (at most 32 per pass, read from L2 as the B operand).
