@@ -83,7 +83,9 @@ __device__ __forceinline__ float unord(uint32_t u) {
 // K-th largest order-preserving key (ord of the logit) is found bit by bit
 // from the top, each bit one compare whose ballot, masked to the remaining
 // candidates, gives a scalar count; keys above it are taken, and of the keys
-// equal to it the lowest expert indices fill the rest.  A taken expert's
+// equal to it the lowest expert indices fill the rest.  The bits stop as soon
+// as the remaining candidates are exactly as many as still needed (for
+// distinct logits after about a dozen bits).  A taken expert's
 // output slot is its rank among the taken (a larger logit first, equal
 // logits by the lower index): the same selection and order as K rounds of
 // arg-max.  Renormalised weights divide by the sum of the taken
@@ -118,6 +120,10 @@ __device__ __forceinline__ void softmax_topk_radix(const float* slog, int64_t t0
     const float inv = 1.0f / wave_fsum(ls);
     int need = K;
     for (int bit = 31; bit >= 0; --bit) {
+      int cc = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) cc += __popcll(cand[j]);
+      if (cc == need) break;  // every remaining candidate is among the K: take them all below
       uint64_t hi[NPL];
       int c1 = 0;
 #pragma unroll
