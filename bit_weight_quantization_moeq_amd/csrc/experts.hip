@@ -598,40 +598,55 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row (a row: 32 lanes of one wave)
     static_assert(kChunks == 32, "one row per half wave");
     const int nct = (C + kTcols - 1) / kTcols;
-#pragma unroll 4
-    for (int u = 0; u < kBM * kChunks / kThreads; ++u) {
-      const int i = threadIdx.x + u * kThreads, r = i / kChunks, k4 = i - r * kChunks;
-      const int c = c0 + 4 * k4;
-      float share = 0.0f;
-      if (r < nrows && c < C) {
-        const int64_t p = row0 + r;
-        const float w = sw[r];
-        const float4 a4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
-        const float4 g4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + c);
-        const float4 u4 = *reinterpret_cast<const float4*>(gu_save + p * 2 * C + C + c);
-        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w},
-                    uv[4] = {u4.x, u4.y, u4.z, u4.w};
-        float dg[4], du[4], hf[4];
+    // Eight rows' g and u loads are issued together before any of them is
+    // used (a row or columns past the end load row 0 of the tile, column c0,
+    // and are masked below), so a wave waits for memory once per eight rows
+    // instead of once per row.
+    constexpr int kIters = kBM * kChunks / kThreads, kGroup = 8;
+    static_assert(kIters % kGroup == 0, "whole groups");
+    for (int u0 = 0; u0 < kIters; u0 += kGroup) {
+      float4 g4[kGroup], u4[kGroup];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
-          const float dv = w * av[e];
-          du[e] = dv * gv[e] * sg;
-          dg[e] = dv * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
-          hf[e] = gv[e] * uv[e] * sg;  // the forward's h before rounding, same operations
-        }
-        const uint32_t h01 = pack_bf16x2(hf[0], hf[1]), h23 = pack_bf16x2(hf[2], hf[3]);
-        const float hv[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u),
-                             __uint_as_float(h23 << 16), __uint_as_float(h23 & 0xffff0000u)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) share += av[e] * hv[e];
-        uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
-        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-        *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+      for (int j = 0; j < kGroup; ++j) {
+        const int i = threadIdx.x + (u0 + j) * kThreads, r = i / kChunks, c = c0 + 4 * (i - r * kChunks);
+        const bool in = r < nrows && c < C;
+        const float* gp = gu_save + (int64_t)(row0 + (in ? r : 0)) * 2 * C + (in ? c : c0);
+        g4[j] = *reinterpret_cast<const float4*>(gp);
+        u4[j] = *reinterpret_cast<const float4*>(gp + C);
       }
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) share += __shfl_xor(share, o, 64);
-      if (k4 == 0 && r < nrows) gw_part[(int64_t)(row0 + r) * nct + ct] = share;
+      for (int j = 0; j < kGroup; ++j) {
+        const int i = threadIdx.x + (u0 + j) * kThreads, r = i / kChunks, k4 = i - r * kChunks;
+        const int c = c0 + 4 * k4;
+        float share = 0.0f;
+        if (r < nrows && c < C) {
+          const int64_t p = row0 + r;
+          const float w = sw[r];
+          const float4 a4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w}, gv[4] = {g4[j].x, g4[j].y, g4[j].z, g4[j].w},
+                      uv[4] = {u4[j].x, u4[j].y, u4[j].z, u4[j].w};
+          float dg[4], du[4], hf[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
+            const float dv = w * av[e];
+            du[e] = dv * gv[e] * sg;
+            dg[e] = dv * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+            hf[e] = gv[e] * uv[e] * sg;  // the forward's h before rounding, same operations
+          }
+          const uint32_t h01 = pack_bf16x2(hf[0], hf[1]), h23 = pack_bf16x2(hf[2], hf[3]);
+          const float hv[4] = {__uint_as_float(h01 << 16), __uint_as_float(h01 & 0xffff0000u),
+                               __uint_as_float(h23 << 16), __uint_as_float(h23 & 0xffff0000u)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) share += av[e] * hv[e];
+          uint16_t* o = static_cast<uint16_t*>(out) + p * 2 * C + c;
+          *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(o + C) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) share += __shfl_xor(share, o, 64);
+        if (k4 == 0 && r < nrows) gw_part[(int64_t)(row0 + r) * nct + ct] = share;
+      }
     }
     return;
   }
