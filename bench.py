@@ -471,10 +471,27 @@ def backward_record(torch, moeq, syn, s, qg, qd, x, idx, wts, dev, reps=10):
     ms = timed(torch, lambda: moeq.moeq_experts_backward(x, idx, wts, qg, qd, dout, grad_hidden=gx,
                                                          grad_weights=gw, workspace=ws), reps)
     flops = 10.0 * T * s.K * s.H * s.I
+    # the training pair that keeps g and u: the forward writes them beside its
+    # output, the backward skips the recompute (the same gradients, bit for bit)
+    gsv = torch.empty((T * s.K, 2 * s.I), dtype=torch.float32, device=dev)
+    out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+    fws = torch.empty(moeq.moeq_experts_forward_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8, device=dev)
+    save_ms = timed(torch, lambda: moeq.moeq_experts_forward_save(x, idx, wts, qg, qd, out=out, gu_saved=gsv,
+                                                                  workspace=fws), reps)
+    sws = torch.empty(moeq.moeq_experts_backward_saved_workspace_bytes(T, s.K, qg, qd), dtype=torch.uint8,
+                      device=dev)
+    saved_ms = timed(torch, lambda: moeq.moeq_experts_backward_saved(idx, wts, qg, qd, gsv, dout, grad_hidden=gx,
+                                                                     grad_weights=gw, workspace=sws), reps)
+    sflops = 6.0 * T * s.K * s.H * s.I
     return {"workload": f"{s.name}-shaped layer, T={T}, incoming gradient ~ N(0, 1) bf16",
             "ms": ms, "tokens_per_s": T / (ms * 1e-3), "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "flops": "10 T K H I (gate_up recompute 4, down^T 2, gate_up^T 4)"}
+            "flops": "10 T K H I (gate_up recompute 4, down^T 2, gate_up^T 4)",
+            "saved_pre_activations": {
+                "forward_save_ms": save_ms, "backward_ms": saved_ms,
+                "TFLOPs": sflops / (saved_ms * 1e-3) / 1e12,
+                "mfma_frac": sflops / (saved_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "flops": "6 T K H I (down^T 2, gate_up^T 4)", "saved_bytes": 8 * T * s.K * s.I}}
 
 
 def router_record(torch, moeq, syn, s, x, dev, copy_GBps, reps=20):

@@ -89,6 +89,9 @@ def _load():
         "moeq_router_route": (I32, [P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, SZ, P]),
         "moeq_experts_forward_routed": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, P, P, SZ, P]),
         "moeq_experts_forward_noalloc": (I32, [P, P, P, I32, I32, QP, QP, P, P]),
+        "moeq_experts_forward_save": (I32, [P, P, P, I32, I32, QP, QP, P, P, P, SZ, P]),
+        "moeq_experts_backward_saved_workspace_bytes": (SZ, [I32, I32, QP, QP]),
+        "moeq_experts_backward_saved": (I32, [P, P, I32, I32, QP, QP, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -512,6 +515,81 @@ def moeq_experts_backward(hidden, top_k_index, top_k_weights, gate_up, down, gra
                                      ctypes.byref(gu), ctypes.byref(dn), _ptr(grad_out), _ptr(grad_hidden),
                                      _ptr(grad_weights), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
            "moeq_experts_backward")
+    return grad_hidden, grad_weights
+
+
+def moeq_experts_forward_save(hidden, top_k_index, top_k_weights, gate_up, down, out=None, gu_saved=None,
+                              workspace=None, stream=None):
+    """:func:`moeq_experts_forward` that also keeps the fp32 gate and up
+    pre-activations of every routed assignment for
+    :func:`moeq_experts_backward_saved`; returns ``(out bf16 [T, H],
+    gu_saved fp32 [T*K, 2I])`` (rows in the expert-major order of the
+    routing; rows past the routed count are not written)."""
+    T, H, K = _routed_inputs(hidden, top_k_index, top_k_weights)
+    if out is not None:
+        _dev(out, torch.bfloat16, "out", (T, H))
+    wt = _forward_weights(gate_up, down, H)
+    I2 = gate_up.rows
+    if gu_saved is not None:
+        _dev(gu_saved, torch.float32, "gu_saved", (T * K, I2))
+    dev = _on_device("moeq_experts_forward_save", hidden, top_k_index, top_k_weights, out, gu_saved, *wt)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if gu_saved is None:
+        gu_saved = torch.empty((T * K, I2), dtype=torch.float32, device=dev)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
+    lib = _load()
+    need = int(lib.moeq_experts_forward_workspace_bytes(T, K, ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, dev)
+    _check(lib.moeq_experts_forward_save(_ptr(hidden), _ptr(top_k_index), _ptr(top_k_weights), T, K,
+                                         ctypes.byref(gu), ctypes.byref(dn), _ptr(out), _ptr(gu_saved),
+                                         _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+           "moeq_experts_forward_save")
+    return out, gu_saved
+
+
+def moeq_experts_backward_saved_workspace_bytes(T, K, gate_up, down):
+    gu, dn = gate_up._c(allow_host=True), down._c(allow_host=True)
+    return int(_load().moeq_experts_backward_saved_workspace_bytes(int(T), int(K), ctypes.byref(gu),
+                                                                   ctypes.byref(dn)))
+
+
+def moeq_experts_backward_saved(top_k_index, top_k_weights, gate_up, down, gu_saved, grad_out, grad_hidden=None,
+                                grad_weights=None, workspace=None, stream=None):
+    """:func:`moeq_experts_backward` from the pre-activations that
+    :func:`moeq_experts_forward_save` kept (``gu_saved`` fp32 ``[T*K, 2I]``),
+    with no recompute of the gate_up GEMM; the same gradients bit for bit.
+    Returns ``(grad_hidden bf16 [T, H], grad_weights fp32 [T, K])``."""
+    if not isinstance(grad_out, torch.Tensor) or grad_out.dim() != 2:
+        raise ValueError("grad_out must be a 2-D tensor")
+    T, H = grad_out.shape
+    _dev(grad_out, torch.bfloat16, "grad_out", (T, H))
+    _dev(top_k_index, torch.int32, "top_k_index")
+    if top_k_index.dim() != 2 or top_k_index.shape[0] != T:
+        raise ValueError(f"top_k_index must have shape ({T}, K), got {tuple(top_k_index.shape)}")
+    K = top_k_index.shape[1]
+    _dev(top_k_weights, torch.float32, "top_k_weights", (T, K))
+    wt = _forward_weights(gate_up, down, H)
+    _dev(gu_saved, torch.float32, "gu_saved", (T * K, gate_up.rows))
+    if grad_hidden is not None:
+        _dev(grad_hidden, torch.bfloat16, "grad_hidden", (T, H))
+    if grad_weights is not None:
+        _dev(grad_weights, torch.float32, "grad_weights", (T, K))
+    dev = _on_device("moeq_experts_backward_saved", top_k_index, top_k_weights, gu_saved, grad_out, grad_hidden,
+                     grad_weights, *wt)
+    if grad_hidden is None:
+        grad_hidden = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if grad_weights is None:
+        grad_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    gu, dn = gate_up._desc(), down._desc()  # validated by the two checks above
+    lib = _load()
+    need = int(lib.moeq_experts_backward_saved_workspace_bytes(T, K, ctypes.byref(gu), ctypes.byref(dn)))
+    workspace = _workspace(workspace, need, dev)
+    _check(lib.moeq_experts_backward_saved(_ptr(top_k_index), _ptr(top_k_weights), T, K, ctypes.byref(gu),
+                                           ctypes.byref(dn), _ptr(gu_saved), _ptr(grad_out), _ptr(grad_hidden),
+                                           _ptr(grad_weights), _ptr(workspace), workspace.numel(),
+                                           _stream(stream, dev)),
+           "moeq_experts_backward_saved")
     return grad_hidden, grad_weights
 
 

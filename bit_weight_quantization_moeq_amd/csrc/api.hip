@@ -282,6 +282,36 @@ moeq_status moeq_experts_forward_timed(const uint16_t* x, const int32_t* idx, co
                                              reinterpret_cast<hipEvent_t const*>(stage_events)));
 }
 
+moeq_status check_backward_shapes(int32_t T, int32_t K, const moeq_qweight* gu, const moeq_qweight* dn);
+
+moeq_status moeq_experts_forward_save(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,
+                                      int32_t K, const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
+                                      float* gu_saved, void* workspace, size_t workspace_bytes, void* stream) {
+  // the backward's shape limits, so that what is saved can always be used
+  moeq_status st = check_backward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!x || !idx || !wts || !out || !gu_saved) return MOEQ_EINVAL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(gu_saved)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const Layout L = layout((int64_t)T * K, E, I, H);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  if (!aligned16(workspace)) return MOEQ_EALIGN;
+  ForwardArgs a;
+  a.x = x; a.idx = idx; a.wts = wts;
+  a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
+  a.format = gu->format;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales; a.gu_c = gu->scale_codes;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
+  a.out = out;
+  a.rb = route_buffers(workspace, L);
+  a.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h);
+  a.y = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.y);
+  a.routed = false;
+  a.gu_save = gu_saved;
+  return device_status(launch_experts_forward(a, static_cast<hipStream_t>(stream), nullptr));
+}
+
 moeq_status moeq_experts_forward_noalloc(const uint16_t* x, const int32_t* idx, const float* wts, int32_t T,
                                          int32_t K, const moeq_qweight* gu, const moeq_qweight* dn, uint16_t* out,
                                          void* stream) {
@@ -331,18 +361,18 @@ moeq_status moeq_experts_forward_routed(const uint16_t* x, const int32_t* idx, c
 }
 
 // Backward workspace: the routing buffers, then T1's grad_w shares fp32
-// [n][column tiles of I], g|u fp32 [n][2I], dx fp32 [n][H] and dg|du bf16
-// [n][2I], 256-B aligned.
+// [n][column tiles of I], g|u fp32 [n][2I] (not when the caller holds them),
+// dx fp32 [n][H] and dg|du bf16 [n][2I], 256-B aligned.
 struct BwLayout {
   Layout route;
   size_t gwp, gu, dx, dgu, total;
 };
-BwLayout bw_layout(int64_t n, int32_t E, int64_t I, int64_t H) {
+BwLayout bw_layout(int64_t n, int32_t E, int64_t I, int64_t H, bool with_gu = true) {
   BwLayout L;
   L.route = layout(n, E, 0, 0);
   size_t o = L.route.total;
   L.gwp = o; o += up(sizeof(float) * (size_t)(n * backward_col_tiles((int32_t)I)));
-  L.gu = o;  o += up(sizeof(float) * (size_t)(n * 2 * I));
+  L.gu = o;  o += with_gu ? up(sizeof(float) * (size_t)(n * 2 * I)) : 0;
   L.dx = o;  o += up(sizeof(float) * (size_t)(n * H));
   L.dgu = o; o += up(sizeof(uint16_t) * (size_t)(n * 2 * I));
   L.total = o;
@@ -387,6 +417,42 @@ moeq_status moeq_experts_backward(const uint16_t* x, const int32_t* idx, const f
   a.rb = route_buffers(workspace, L.route);
   a.gw_part = reinterpret_cast<float*>(w + L.gwp);
   a.gu_save = reinterpret_cast<float*>(w + L.gu);
+  a.dx = reinterpret_cast<float*>(w + L.dx);
+  a.dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
+  return device_status(launch_experts_backward(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t moeq_experts_backward_saved_workspace_bytes(int32_t T, int32_t K, const moeq_qweight* gu,
+                                                   const moeq_qweight* dn) {
+  if (check_backward_shapes(T, K, gu, dn) != MOEQ_OK) return 0;
+  return bw_layout((int64_t)T * K, gu->num_experts, gu->rows / 2, gu->cols, false).total;
+}
+
+moeq_status moeq_experts_backward_saved(const int32_t* idx, const float* wts, int32_t T, int32_t K,
+                                        const moeq_qweight* gu, const moeq_qweight* dn, const float* gu_saved,
+                                        const uint16_t* dout, uint16_t* grad_x, float* grad_w, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  moeq_status st = check_backward_shapes(T, K, gu, dn);
+  if (st != MOEQ_OK) return st;
+  if (T == 0) return MOEQ_OK;
+  if (!idx || !wts || !gu_saved || !dout || !grad_x || !grad_w) return MOEQ_EINVAL;
+  if (!aligned16(gu_saved) || !aligned16(dout) || !aligned16(grad_x)) return MOEQ_EALIGN;
+  const int32_t I = gu->rows / 2, H = gu->cols, E = gu->num_experts;
+  const BwLayout L = bw_layout((int64_t)T * K, E, I, H, false);
+  if (!workspace || workspace_bytes < L.total) return MOEQ_EWORKSPACE;
+  if (!aligned16(workspace)) return MOEQ_EALIGN;
+  char* w = static_cast<char*>(workspace);
+  BackwardArgs a;
+  a.x = nullptr; a.idx = idx; a.wts = wts; a.dout = dout;
+  a.T = T; a.K = K; a.E = E; a.H = H; a.I = I;
+  a.format = gu->format;
+  a.gu_q = gu->qdata; a.gu_s = gu->scales; a.gu_c = gu->scale_codes;
+  a.dn_q = dn->qdata; a.dn_s = dn->scales; a.dn_c = dn->scale_codes;
+  a.grad_x = grad_x; a.grad_w = grad_w;
+  a.rb = route_buffers(workspace, L.route);
+  a.gw_part = reinterpret_cast<float*>(w + L.gwp);
+  a.gu_save = const_cast<float*>(gu_saved);  // read only: the recompute that writes it is skipped
+  a.recompute = false;
   a.dx = reinterpret_cast<float*>(w + L.dx);
   a.dgu = reinterpret_cast<uint16_t*>(w + L.dgu);
   return device_status(launch_experts_backward(a, static_cast<hipStream_t>(stream)));

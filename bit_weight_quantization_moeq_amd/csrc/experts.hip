@@ -700,7 +700,7 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, a.rb.offsets,
-                                         a.rb.tile_start, a.rb.perm, a.h, nullptr);
+                                         a.rb.tile_start, a.rb.perm, a.h, a.gu_save);
   if (ev) (void)hipEventRecord(ev[2], s);
   // y rows rounded to bf16 here (the fp32 workspace buffer holds them)
   uint16_t* y16 = reinterpret_cast<uint16_t*>(a.y);
@@ -715,7 +715,7 @@ hipError_t launch_tiled(const ForwardArgs& a, hipStream_t s, hipEvent_t const* e
 template <int FMT>
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* ev) {
   if (ev) (void)hipEventRecord(ev[0], s);
-  return a.T * a.K <= kDecodeMax ? launch_experts_decode(a, s, ev) : launch_tiled<FMT>(a, s, ev);
+  return a.T * a.K <= kDecodeMax && !a.gu_save ? launch_experts_decode(a, s, ev) : launch_tiled<FMT>(a, s, ev);
 }
 
 template <int FMT>
@@ -730,8 +730,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
   const uint8_t* guq = static_cast<const uint8_t*>(a.gu_q);
   const uint8_t* dnq = static_cast<const uint8_t*>(a.dn_q);
   const RouteBuffers& r = a.rb;
-  g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, r.offsets, r.tile_start,
-                                         r.perm, nullptr, a.gu_save);
+  if (a.recompute)
+    g1_kernel<FMT><<<g1, kThreads, 0, s>>>(a.x, a.K, a.E, a.H, a.I, guq, a.gu_s, a.gu_c, r.offsets, r.tile_start,
+                                           r.perm, nullptr, a.gu_save);
   tgemm_kernel<FMT, 1><<<t1, kThreads, 0, s>>>(a.dout, a.K, a.E, a.H, a.I, dnq, a.dn_s, a.dn_c, r.offsets,
                                                r.tile_start, r.perm, a.wts, a.gu_save, a.dgu, a.gw_part);
   gradw_kernel<<<(n + kWaves - 1) / kWaves, kThreads, 0, s>>>(a.gw_part, r.slot, n, backward_col_tiles(a.I),

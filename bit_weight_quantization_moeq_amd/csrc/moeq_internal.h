@@ -113,6 +113,8 @@ struct ForwardArgs {
   float* y;                 // [T*K][H]: bf16 expert-sorted rows (tiled path) or fp32 (few-assignment path)
   bool routed;              // rb.offsets / perm / slot already hold the routing of idx (only
                             // tile_start is derived here)
+  float* gu_save = nullptr; // [T*K][2I] fp32, expert-sorted rows: g | u kept for the backward
+                            // (non-null: the tiled path for every batch size)
 };
 // events: NULL or 5 events recorded at the stage boundaries.
 hipError_t launch_experts_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t const* events);
@@ -141,6 +143,7 @@ struct BackwardArgs {
   RouteBuffers rb;
   float* gw_part;           // [n][backward_col_tiles(I)] fp32, sorted rows: T1's shares of grad_w
   float* gu_save;           // [n][2I] fp32, sorted rows
+  bool recompute = true;    // false: gu_save already holds the forward's g | u (no gate_up GEMM)
   float* dx;                // [n][H] fp32, sorted rows
   uint16_t* dgu;            // [n][2I] bf16, sorted rows
 };

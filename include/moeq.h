@@ -274,6 +274,42 @@ moeq_status moeq_experts_backward(const uint16_t *hidden_bf16, const int32_t *to
                                   void *stream);
 
 /*
+ * Training pair without the backward's recompute of the gate_up GEMM, for
+ * adapter training over frozen quantized experts ("MoE Expert Quantization",
+ * Axolotl docs, Expert LoRA targeting; Axolotl issue #3787, Use case) when
+ * the memory for the pre-activations is there.  moeq_experts_forward_save is
+ * moeq_experts_forward that also writes, for every routed assignment, the
+ * fp32 g = gate[e] x_t and u = up[e] x_t; moeq_experts_backward_saved takes
+ * them in place of its recompute.  The chain rule, roundings and order are
+ * moeq_experts_backward's, and both calls group the assignments in the same
+ * deterministic order, so the gradients equal moeq_experts_backward's bit
+ * for bit.
+ *   gu_saved  fp32 [T*K][2I], caller-owned, 16-byte aligned: row p holds g
+ *             (columns 0..I-1) then u (I..2I-1) of the p-th assignment in
+ *             the expert-major stable order of moeq_route_buckets' perm;
+ *             rows past the routed count are not written.  It must come from
+ *             moeq_experts_forward_save with the same top_k_index, hidden
+ *             states and gate_up (not checked).
+ * moeq_experts_forward_save takes the tiled path for every batch size (for
+ * T*K <= 512 moeq_experts_forward takes the few-assignment path, whose
+ * output then agrees within rounding, not bit for bit); its workspace is
+ * moeq_experts_forward_workspace_bytes.  The backward needs no hidden
+ * states; its workspace, moeq_experts_backward_saved_workspace_bytes, has
+ * no g|u region.  Both return MOEQ_ESHAPE where moeq_experts_backward does.
+ */
+moeq_status moeq_experts_forward_save(const uint16_t *hidden_bf16, const int32_t *top_k_index,
+                                      const float *top_k_weights, int32_t T, int32_t K,
+                                      const moeq_qweight *gate_up, const moeq_qweight *down, uint16_t *out_bf16,
+                                      float *gu_saved, void *workspace, size_t workspace_bytes, void *stream);
+size_t moeq_experts_backward_saved_workspace_bytes(int32_t T, int32_t K, const moeq_qweight *gate_up,
+                                                   const moeq_qweight *down);
+moeq_status moeq_experts_backward_saved(const int32_t *top_k_index, const float *top_k_weights, int32_t T,
+                                        int32_t K, const moeq_qweight *gate_up, const moeq_qweight *down,
+                                        const float *gu_saved, const uint16_t *grad_out_bf16,
+                                        uint16_t *grad_hidden_bf16, float *grad_weights, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
  * Router front-end producing the experts' (top_k_index, top_k_weights): the
  * gate weight mlp.gate.weight stays bf16 beside the quantized experts
  * ("MoE Expert Quantization", Axolotl docs, Expert LoRA targeting;

@@ -132,3 +132,18 @@ def test_router_outputs_must_match():
 def test_copy_rejects_unpinned_host_memory():
     with pytest.raises(ValueError):
         moeq.moeq_qweight_copy_async(_nf4(), _nf4())
+
+
+def test_saved_pair_buffers_must_match():
+    gu, dn = _nf4(R=2 * 64, C=C), _nf4(R=C, C=64)
+    x, idx, w = _routed()
+    T, K = idx.shape
+    g = torch.empty_like(x)
+    with pytest.raises(ValueError):  # one row short of T*K
+        moeq.moeq_experts_forward_save(x, idx, w, gu, dn, gu_saved=torch.empty((T * K - 1, 2 * 64)))
+    with pytest.raises(ValueError):  # one column short of 2I
+        moeq.moeq_experts_backward_saved(idx, w, gu, dn, torch.empty((T * K, 2 * 64 - 1)), g)
+    with pytest.raises(ValueError):  # grad_out with fewer tokens than the routing
+        moeq.moeq_experts_backward_saved(idx, w, gu, dn, torch.empty((T * K, 2 * 64)), g[:2].contiguous())
+    with pytest.raises(TypeError):  # bf16 pre-activations
+        moeq.moeq_experts_backward_saved(idx, w, gu, dn, torch.empty((T * K, 2 * 64), dtype=torch.bfloat16), g)
