@@ -504,8 +504,11 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
   vstage(0, 0);
   wstore(ca, 0);  // waits for the codes (and the DMA issued before them)
   wfetch(ca, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // as at the end of every step: only the codes just requested (used after
+  // the first MFMA of step 0) stay in flight
+  __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<kWLoads>);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   auto frags = [&](int buf, int s4, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
