@@ -585,8 +585,29 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
     // accumulator layout each such load touched 32 rows).  Per element
     // dh = w * acc; the row's share of grad_w adds acc * h over the thread's
     // columns in order, then over the row's 32 lanes in a fixed tree.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row (a row: 32 lanes of one wave)
+    static_assert(kChunks == 32, "one row per half wave");
+    const int nct = (C + kTcols - 1) / kTcols;
+    // The g and u loads go eight rows at a time, one group ahead: group 0
+    // before the accumulators are staged, group i + 1 before group i is used
+    // (a row or columns past the end load row 0 of the tile, column c0, and
+    // are masked below).
+    constexpr int kIters = kBM * kChunks / kThreads, kGroup = 8, kGroups = kIters / kGroup;
+    static_assert(kIters % kGroup == 0, "whole groups");
+    float4 g4[2][kGroup], u4[2][kGroup];
+    auto gload = [&](int u0, float4 (&gg)[kGroup], float4 (&uu)[kGroup]) {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const int i = threadIdx.x + (u0 + j) * kThreads, r = i / kChunks, c = c0 + 4 * (i - r * kChunks);
+        const bool in = r < nrows && c < C;
+        const float* gp = gu_save + (int64_t)(row0 + (in ? r : 0)) * 2 * C + (in ? c : c0);
+        gg[j] = *reinterpret_cast<const float4*>(gp);
+        uu[j] = *reinterpret_cast<const float4*>(gp + C);
+      }
+    };
+    gload(0, g4[0], u4[0]);
+    // The last K step ended in a barrier after every wave's fragment reads
+    // and DMAs had completed, so the LDS array is free here.
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -597,37 +618,24 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(const uint16_t* __restr
           *reinterpret_cast<float4*>(smem + (tw + 32 * b + l32) * kOutPitch + 4 * (cw + 32 * m + 8 * q + 4 * hh)) =
               make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         }
-    __syncthreads();
-    constexpr int kChunks = kTcols / 4;  // 4-column chunks of a tile row (a row: 32 lanes of one wave)
-    static_assert(kChunks == 32, "one row per half wave");
-    const int nct = (C + kTcols - 1) / kTcols;
-    // Eight rows' g and u loads are issued together before any of them is
-    // used (a row or columns past the end load row 0 of the tile, column c0,
-    // and are masked below), so a wave waits for memory once per eight rows
-    // instead of once per row.
-    constexpr int kIters = kBM * kChunks / kThreads, kGroup = 8;
-    static_assert(kIters % kGroup == 0, "whole groups");
-    for (int u0 = 0; u0 < kIters; u0 += kGroup) {
-      float4 g4[kGroup], u4[kGroup];
+    __builtin_amdgcn_s_waitcnt(kVmcntLgkmWait<63>);  // this wave's LDS stores only
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      if (gi + 1 < kGroups) gload((gi + 1) * kGroup, g4[(gi + 1) & 1], u4[(gi + 1) & 1]);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
-        const int i = threadIdx.x + (u0 + j) * kThreads, r = i / kChunks, c = c0 + 4 * (i - r * kChunks);
-        const bool in = r < nrows && c < C;
-        const float* gp = gu_save + (int64_t)(row0 + (in ? r : 0)) * 2 * C + (in ? c : c0);
-        g4[j] = *reinterpret_cast<const float4*>(gp);
-        u4[j] = *reinterpret_cast<const float4*>(gp + C);
-      }
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const int i = threadIdx.x + (u0 + j) * kThreads, r = i / kChunks, k4 = i - r * kChunks;
+        const int i = threadIdx.x + (gi * kGroup + j) * kThreads, r = i / kChunks, k4 = i - r * kChunks;
         const int c = c0 + 4 * k4;
         float share = 0.0f;
         if (r < nrows && c < C) {
           const int64_t p = row0 + r;
           const float w = sw[r];
           const float4 a4 = *reinterpret_cast<const float4*>(smem + r * kOutPitch + 16 * k4);
-          const float av[4] = {a4.x, a4.y, a4.z, a4.w}, gv[4] = {g4[j].x, g4[j].y, g4[j].z, g4[j].w},
-                      uv[4] = {u4[j].x, u4[j].y, u4[j].z, u4[j].w};
+          const float4 gq = g4[gi & 1][j], uq = u4[gi & 1][j];
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w}, gv[4] = {gq.x, gq.y, gq.z, gq.w},
+                      uv[4] = {uq.x, uq.y, uq.z, uq.w};
           float dg[4], du[4], hf[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
